@@ -1,0 +1,114 @@
+"""Seeded synthetic inputs for the attention workloads.
+
+This module only draws random numbers and rounds them to the storage type.
+It holds none of the attention arithmetic, so both the fp64 oracle (``oracle/``)
+and the HIP path (``exact_attention_14_amd``) may take their inputs from it
+without sharing any of the method's code.
+
+Recipe (the same for every workload):
+  * generator: numpy ``default_rng(seed)`` (PCG64);
+  * Q, K, V and then (for the backward workload) the upstream gradient dO are
+    drawn, in that order, as float32 standard normals of shape [B, H, N, d]
+    in C order;
+  * each float32 tensor is rounded once, to nearest-even, to fp16 or bf16;
+  * the causal outlier workload then picks round(0.01 * N) distinct key rows per
+    (b, h), b-major then h, uniformly without replacement from the same
+    generator, and multiplies those K rows by 8 (a power of two, so exact).
+
+The pages measure on model-shaped random activations (LLaMA-7B / LLaMA-13B
+attention shapes, and a long-sequence window case); i.i.d. N(0, 1) inputs of the
+same shapes stand in for them.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+import torch
+
+_TORCH_DTYPES = {"f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str          # "f16" or "bf16": storage type of Q, K, V, O (and dO)
+    mask: str           # "none", "causal" or "sliding"
+    window_left: int    # read only for "sliding"
+    window_right: int   # read only for "sliding"
+    seed: int
+    backward: bool = False       # also draw dO (forward + backward workload)
+    outlier_frac: float = 0.0    # fraction of K rows per head scaled by outlier_mul
+    outlier_mul: float = 1.0
+
+    @property
+    def scale(self) -> float:
+        """Score scale 1/sqrt(d), as the float32 value handed to the kernels."""
+        return float(np.float32(1.0 / math.sqrt(self.d)))
+
+    @property
+    def torch_dtype(self) -> torch.dtype:
+        return _TORCH_DTYPES[self.dtype]
+
+
+# The five workloads, named by what they are.
+SINGLE_HEAD_N256 = Workload("b1h1n256d64_f16_full", 1, 1, 256, 64, "f16", "none", 0, 0, seed=1)
+FULL_N4096 = Workload("b4h32n4096d128_bf16_full", 4, 32, 4096, 128, "bf16", "none", 0, 0, seed=2)
+CAUSAL_OUTLIERS_N4096 = Workload("b4h32n4096d128_bf16_causal_outlierkeys", 4, 32, 4096, 128, "bf16",
+                                 "causal", 0, 0, seed=3, outlier_frac=0.01, outlier_mul=8.0)
+LLAMA13B_CAUSAL_FWDBWD = Workload("b8h40n4096d128_f16_causal_fwdbwd", 8, 40, 4096, 128, "f16",
+                                  "causal", 0, 0, seed=4, backward=True)
+SLIDING_N32768 = Workload("b1h40n32768d128_bf16_sliding4096", 1, 40, 32768, 128, "bf16",
+                          "sliding", 4096, 0, seed=5)
+
+ALL = (SINGLE_HEAD_N256, FULL_N4096, CAUSAL_OUTLIERS_N4096, LLAMA13B_CAUSAL_FWDBWD, SLIDING_N32768)
+BY_NAME = {w.name: w for w in ALL}
+
+
+def _round(x32: np.ndarray, dtype: str) -> torch.Tensor:
+    """Round a float32 array once, to nearest-even, to the storage type."""
+    return torch.from_numpy(x32).to(_TORCH_DTYPES[dtype])
+
+
+def draw(B: int, H: int, N: int, d: int, dtype: str, seed: int, *, with_do: bool = False,
+         outlier_frac: float = 0.0, outlier_mul: float = 1.0) -> dict:
+    """Draw Q, K, V (and dO) on the host, rounded to ``dtype``.
+
+    Returns a dict of CPU torch tensors of shape [B, H, N, d]; with outliers it
+    also holds ``outlier_rows`` (an int64 array [B, H, n_out]) for reference.
+    """
+    rng = np.random.default_rng(seed)
+    shape = (B, H, N, d)
+    out = {}
+    for key in ("q", "k", "v") + (("do",) if with_do else ()):
+        out[key] = _round(rng.standard_normal(shape, dtype=np.float32), dtype)
+    if outlier_frac > 0.0:
+        n_out = int(round(outlier_frac * N))
+        rows = np.empty((B, H, n_out), dtype=np.int64)
+        for b in range(B):
+            for h in range(H):
+                rows[b, h] = rng.choice(N, size=n_out, replace=False)
+        kk = out["k"]
+        mul = torch.tensor(outlier_mul, dtype=kk.dtype)
+        for b in range(B):
+            for h in range(H):
+                idx = torch.from_numpy(rows[b, h])
+                kk[b, h, idx] = kk[b, h, idx] * mul
+        out["outlier_rows"] = rows
+    return out
+
+
+def make_inputs(w: Workload) -> dict:
+    """The seeded inputs of a named workload (CPU tensors)."""
+    return draw(w.B, w.H, w.N, w.d, w.dtype, w.seed, with_do=w.backward,
+                outlier_frac=w.outlier_frac, outlier_mul=w.outlier_mul)
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    """Exact widening of an fp16/bf16 CPU tensor to a float64 numpy array."""
+    return t.detach().to("cpu").to(torch.float64).numpy()
