@@ -1,0 +1,196 @@
+"""Benchmark of the exact-attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one attn_fwd call over the whole batch of the workload (host plan,
+Q load, K/V streaming, score products, masking, online softmax, output
+products, epilogue: the whole forward path), with inputs already resident in
+device memory.  The default workload is B=4, H=32, N=4096, d=128, bf16, no
+mask.  Prints one JSON line with the throughput in TFLOP/s of algorithmic work
+(4*d FLOP per allowed (query, key) pair), the roofline position of the forward
+kernel (HIP events on the launch stream), and the fp64 CPU oracle timed on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from workloads import BY_NAME, FULL_N4096, make_inputs  # noqa: E402
+
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}  # MI355X dense matrix-core peak
+HBM_PEAK_GBS = 8000.0
+
+
+def allowed_pairs(N: int, mode: str, wl: int, wr: int) -> int:
+    """Number of allowed (query, key) pairs of one head (closed form)."""
+    if mode == "none":
+        return N * N
+    if mode == "causal":
+        return N * (N + 1) // 2
+    wl, wr = min(wl, N), min(wr, N)
+    total = 0
+    # row i: min(i, wl) + 1 + min(N - 1 - i, wr)
+    for i in range(N):
+        total += min(i, wl) + 1 + min(N - 1 - i, wr)
+    return total
+
+
+def fwd_flops(w) -> int:
+    return 4 * w.d * w.B * w.H * allowed_pairs(w.N, w.mask, w.window_left, w.window_right)
+
+
+def mask_arg(w):
+    if w.mask == "none":
+        return None
+    if w.mask == "causal":
+        return "causal"
+    return (w.window_left, w.window_right)
+
+
+def cpu_baseline(w, inp, budget_s: float = 12.0, max_heads: int = 128):
+    """The fp64 oracle as it stands, on whole heads of the workload, until ~budget_s."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from workloads import to_f64
+
+    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done = 0
+    t0 = time.perf_counter()
+    rb = 1024 if w.N > 8192 else w.N
+    while done < min(max_heads, len(heads)):
+        b, h = heads[done]
+        q, k, v = (to_f64(inp[x][b, h]) for x in ("q", "k", "v"))
+        for r0 in range(0, w.N, rb):
+            rows = np.arange(r0, min(w.N, r0 + rb))
+            oracle.forward_rows(rows, q, k, v, w.scale, w.mask, w.window_left, w.window_right)
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = 4 * w.d * done * allowed_pairs(w.N, w.mask, w.window_left, w.window_right)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {len(heads)} heads, all {w.N} rows each (fp64 numpy, S and P "
+                      f"materialised per head), {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=FULL_N4096.name, choices=sorted(BY_NAME))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one device copy of this many MiB (HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the forward shards by head with no exchange, "
+              "so the one-GPU figure is the per-GPU figure", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_attention_14_amd as ea
+
+    w = BY_NAME[args.workload]
+    inp = make_inputs(w)
+    q, k, v = (inp[x].to("cuda") for x in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    mask = mask_arg(w)
+
+    def step():
+        ea.attn_fwd(q, k, v, mask=mask, scale=w.scale, out=o, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_wall = (t1 - t0) * 1e3 / args.steps
+    ms_kernel = ev0.elapsed_time(ev1) / args.steps
+    flops = fwd_flops(w)
+    value = flops / (ms_wall * 1e-3) / 1e12
+    achieved = flops / (ms_kernel * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", f"traffic_{w.name}.json")
+    if os.path.exists(tpath):
+        with open(tpath) as f:
+            tr = json.load(f)
+        if tr.get("kernel_source_sha") == _kernel_source_sha():
+            traffic = tr.get("bytes_per_launch")
+
+    rec = {
+        "metric": "attention fwd TFLOP/s (and % of bf16 MFMA peak) at B4 H32 N4096 d128",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_wall, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded i.i.d. N(0,1) inputs of the workload's shape)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "mask": w.mask,
+                   "window_left": w.window_left, "window_right": w.window_right,
+                   "scale": w.scale, "global_batch": w.B, "seq_len": w.N, "parallelism": "none"},
+        "tokens_per_s": round(w.B * w.N / (ms_wall * 1e-3), 1),
+        "frac_of_peak": round(value / peak, 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "kernel": "fwd_kernel", "kernel_ms": round(ms_kernel, 5),
+                     "flop_per_launch": flops},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(w, inp)
+    print(json.dumps(rec), flush=True)
+
+
+def _kernel_source_sha() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for name in ("fwd_kernel.hip", "device_common.hpp", "plan.hpp"):
+        with open(os.path.join(ROOT, "exact_attention_14_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

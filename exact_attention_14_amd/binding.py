@@ -1,0 +1,198 @@
+"""Thin ctypes binding over libattn.so: argument marshalling only.
+
+The names match the C ABI in ``include/attn.h``.  Every step of the forward and
+backward runs in the library's HIP kernels; this module only checks torch
+tensors, allocates outputs with torch on the tensors' device, and passes raw
+pointers plus torch's current HIP stream.  There is no fallback of any kind:
+if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+_lib = None
+
+ATTN_F16, ATTN_BF16 = 0, 1
+ATTN_MASK_NONE, ATTN_MASK_CAUSAL, ATTN_MASK_SLIDING = 0, 1, 2
+STATUS = {0: "ATTN_OK", 1: "ATTN_E_NULLPTR", 2: "ATTN_E_SHAPE", 3: "ATTN_E_UNSUPPORTED",
+          4: "ATTN_E_MASK", 5: "ATTN_E_SCALE", 6: "ATTN_E_ALIGN", 7: "ATTN_E_ALIAS",
+          8: "ATTN_E_WORKSPACE", 9: "ATTN_E_HIP"}
+
+# Every symbol include/attn.h declares.
+EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str",
+           "attn_fwd_check", "attn_bwd_check", "attn_fwd_tiles", "attn_kv_tile_range",
+           "attn_fwd_workgroup")
+
+
+class AttnError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({message})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libattn.so (built by ``exact_attention_14_amd.build``); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built; run `python -m exact_attention_14_amd.build`")
+    L = ctypes.CDLL(_LIB_PATH)
+    vp, i64, f32, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_float, ctypes.c_int, ctypes.c_size_t
+    p64 = ctypes.POINTER(ctypes.c_int64)
+    L.attn_fwd.argtypes = [i32, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, i32, i64, i64, vp]
+    L.attn_fwd.restype = i32
+    L.attn_fwd_check.argtypes = [i32, vp, vp, vp, vp, vp, i64, i64, i64, i64, f32, i32, i64, i64]
+    L.attn_fwd_check.restype = i32
+    L.attn_bwd.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64,
+                           f32, i32, i64, i64, vp]
+    L.attn_bwd.restype = i32
+    L.attn_bwd_check.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64,
+                                 i64, f32, i32, i64, i64]
+    L.attn_bwd_check.restype = i32
+    L.attn_bwd_workspace_bytes.argtypes = [i32, i64, i64, i64, i64]
+    L.attn_bwd_workspace_bytes.restype = sz
+    L.attn_status_str.argtypes = [i32]
+    L.attn_status_str.restype = ctypes.c_char_p
+    L.attn_fwd_tiles.argtypes = [i64, p64, p64]
+    L.attn_fwd_tiles.restype = i32
+    L.attn_kv_tile_range.argtypes = [i64, i64, i64, i64, i32, i64, i64, p64, p64]
+    L.attn_kv_tile_range.restype = i32
+    L.attn_fwd_workgroup.argtypes = [i64, i64, i64, i32, p64, p64]
+    L.attn_fwd_workgroup.restype = i32
+    _lib = L
+    return L
+
+
+def attn_status_str(status: int) -> str:
+    return lib().attn_status_str(status).decode()
+
+
+def _raise(fn: str, status: int):
+    if status != 0:
+        raise AttnError(fn, status, attn_status_str(status))
+
+
+def mask_args(mask) -> tuple:
+    """None -> none; "causal" -> causal; (window_left, window_right) -> sliding.
+
+    Mirrors the mask argument of the pages' Python interface (P4 "usage"),
+    with an explicit string for causal instead of inferring it from a tensor.
+    """
+    if mask is None or mask == "none":
+        return ATTN_MASK_NONE, 0, 0
+    if mask == "causal":
+        return ATTN_MASK_CAUSAL, 0, 0
+    if isinstance(mask, (tuple, list)) and len(mask) == 2:
+        return ATTN_MASK_SLIDING, int(mask[0]), int(mask[1])
+    raise ValueError(f"mask must be None, 'causal' or (window_left, window_right), got {mask!r}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float16:
+        return ATTN_F16
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected float16 or bfloat16")
+
+
+def _check4(name: str, t: torch.Tensor, ref: torch.Tensor):
+    if t.dim() != 4 or tuple(t.shape) != tuple(ref.shape):
+        raise ValueError(f"{name} must have shape {tuple(ref.shape)}, got {tuple(t.shape)}")
+    if t.dtype != ref.dtype or t.device != ref.device:
+        raise ValueError(f"{name} must be {ref.dtype} on {ref.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous [B, H, N, d]")
+
+
+def _stream_ptr(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, mask=None, scale=None,
+             out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """Forward pass; returns (O, lse).  Inputs: contiguous [B, H, N, d] on a GPU.
+
+    ``scale`` defaults to 1/sqrt(d) (P1 §1).  ``out``/``lse`` may be given to
+    write into preallocated buffers.
+    """
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    _check4("k", k, q)
+    _check4("v", v, q)
+    _check4("q", q, q)
+    if not q.is_cuda:
+        raise ValueError("inputs must be on a GPU")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    mode, wl, wr = mask_args(mask)
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check4("out", out, q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    elif lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, N]")
+    st = lib().attn_fwd(dt, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                        lse.data_ptr(), B, H, N, d, float(scale), mode, wl, wr,
+                        _stream_ptr(q.device))
+    _raise("attn_fwd", st)
+    return out, lse
+
+
+def attn_bwd_workspace_bytes(dtype: torch.dtype, B: int, H: int, N: int, d: int) -> int:
+    dt = ATTN_BF16 if dtype == torch.bfloat16 else ATTN_F16
+    return int(lib().attn_bwd_workspace_bytes(dt, B, H, N, d))
+
+
+def attn_bwd(q, k, v, o, lse, do, *, mask=None, scale=None, workspace=None):
+    """Recomputation backward; returns (dQ, dK, dV) for upstream gradient ``do``."""
+    _check4("q", q, q)
+    for name, t in (("k", k), ("v", v), ("o", o), ("do", do)):
+        _check4(name, t, q)
+    B, H, N, d = q.shape
+    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, H, N]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    mode, wl, wr = mask_args(mask)
+    dt = _dtype_code(q)
+    need = attn_bwd_workspace_bytes(q.dtype, B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    st = lib().attn_bwd(dt, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                        lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                        dv.data_ptr(), workspace.data_ptr(), workspace.numel(), B, H, N, d,
+                        float(scale), mode, wl, wr, _stream_ptr(q.device))
+    _raise("attn_bwd", st)
+    return dq, dk, dv
+
+
+def attn_kv_tile_range(N, q0, block_q, block_k, mode, wl=0, wr=0):
+    lo, hi = ctypes.c_int64(), ctypes.c_int64()
+    st = lib().attn_kv_tile_range(N, q0, block_q, block_k, mode, wl, wr, ctypes.byref(lo),
+                                  ctypes.byref(hi))
+    _raise("attn_kv_tile_range", st)
+    return lo.value, hi.value
+
+
+def attn_fwd_tiles(d):
+    bq, bk = ctypes.c_int64(), ctypes.c_int64()
+    _raise("attn_fwd_tiles", lib().attn_fwd_tiles(d, ctypes.byref(bq), ctypes.byref(bk)))
+    return bq.value, bk.value
+
+
+def attn_fwd_workgroup(wg, n_heads, n_qblk, mode):
+    h, qb = ctypes.c_int64(), ctypes.c_int64()
+    st = lib().attn_fwd_workgroup(wg, n_heads, n_qblk, mode, ctypes.byref(h), ctypes.byref(qb))
+    _raise("attn_fwd_workgroup", st)
+    return h.value, qb.value

@@ -1,0 +1,133 @@
+// plan.hpp -- tile geometry shared by the host planner and the device kernels.
+//
+// Everything here is plain integer arithmetic on sizes; it is compiled both
+// into host code (validation, launch geometry, the host-only query functions)
+// and into the kernels, so the two always agree on which key tiles a query
+// block visits and which workgroup owns which query block.
+//
+// Sources: P1 = ai6s.net/6af30f4d40858c2d8819b6d5.html, P4 =
+// ai6s.net/6a0ed07b662f9a54cb761aa2.html.
+#pragma once
+
+#include <stdint.h>
+
+#if defined(__HIPCC__)
+#define ATTN_HD __host__ __device__ __forceinline__
+#else
+#define ATTN_HD inline
+#endif
+
+namespace attn {
+
+enum MaskMode : int { kNone = 0, kCausal = 1, kSliding = 2 };
+
+// Forward tile shape: 4 wavefronts x 32 query rows, 64-row K/V tiles.
+constexpr int kFwdBlockQ = 128;
+constexpr int kFwdBlockK = 64;
+constexpr int kFwdThreads = 256;
+
+// Backward: the dQ pass mirrors the forward (query-major); the dK/dV pass is
+// key-major with 4 wavefronts x 32 key rows and 64-row query tiles.
+constexpr int kBwdDqBlockQ = 128;
+constexpr int kBwdDqBlockK = 64;
+constexpr int kBwdKvBlockK = 128;
+constexpr int kBwdKvBlockQ = 64;
+constexpr int kBwdThreads = 256;
+
+constexpr int kNumXcd = 8;  // accelerator dies per MI355X, each with its own L2
+
+ATTN_HD int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+ATTN_HD int64_t imin(int64_t a, int64_t b) { return a < b ? a : b; }
+ATTN_HD int64_t imax(int64_t a, int64_t b) { return a > b ? a : b; }
+
+// The allowed key interval [klo, khi) of the query rows [q0, q1) (q1 clipped
+// to N): its union over the rows, per mask rule (P4 "usage" variants; the
+// bounds are the inclusive reading documented in attn.h).  Windows must be
+// clipped to [0, N] by the caller.
+ATTN_HD void allowed_key_hull(int64_t N, int64_t q0, int64_t q1, int mode, int64_t wl, int64_t wr,
+                              int64_t* klo, int64_t* khi) {
+  q1 = imin(q1, N);
+  int64_t lo = 0, hi = N;
+  if (mode == kCausal) {
+    hi = q1;  // last query q1-1 sees keys <= q1-1
+  } else if (mode == kSliding) {
+    lo = imax(0, q0 - wl);
+    hi = imin(N, q1 - 1 + wr + 1);
+  }
+  *klo = lo;
+  *khi = hi;
+}
+
+// Key tiles [lo, hi) of block_k rows that query rows [q0, q0 + block_q) visit
+// (whole-tile skipping, P1 §3.3 optimisation (4)).  Every tile in range holds
+// at least one allowed pair: the hull is an interval of allowed keys.
+ATTN_HD void kv_tile_range(int64_t N, int64_t q0, int64_t block_q, int64_t block_k, int mode,
+                           int64_t wl, int64_t wr, int64_t* lo, int64_t* hi) {
+  int64_t klo, khi;
+  allowed_key_hull(N, q0, q0 + block_q, mode, wl, wr, &klo, &khi);
+  *lo = klo / block_k;
+  *hi = ceil_div(khi, block_k);
+}
+
+// Query tiles [lo, hi) of block_q rows that key rows [k0, k0 + block_k) are
+// visited by (the backward's key-major loop).  Mirror of kv_tile_range.
+ATTN_HD void q_tile_range(int64_t N, int64_t k0, int64_t block_k, int64_t block_q, int mode,
+                          int64_t wl, int64_t wr, int64_t* lo, int64_t* hi) {
+  int64_t k1 = imin(k0 + block_k, N);
+  int64_t qlo = 0, qhi = N;
+  if (mode == kCausal) {
+    qlo = k0;  // key k is seen by queries >= k
+  } else if (mode == kSliding) {
+    qlo = imax(0, k0 - wr);            // query i sees j iff j - wr <= i <= j + wl
+    qhi = imin(N, k1 - 1 + wl + 1);
+  }
+  *lo = qlo / block_q;
+  *hi = ceil_div(qhi, block_q);
+}
+
+// True if every (query, key) pair of query rows [q0, q0 + nq) x key rows
+// [k0, k0 + nk) is allowed and every key is < N, so the tile needs no mask.
+// Query rows >= N are padding whose results are never stored.
+ATTN_HD bool tile_all_allowed(int64_t N, int64_t q0, int64_t nq, int64_t k0, int64_t nk, int mode,
+                              int64_t wl, int64_t wr) {
+  if (k0 + nk > N) return false;
+  int64_t qlast = imin(q0 + nq, N) - 1;
+  if (mode == kCausal) return k0 + nk - 1 <= q0;
+  if (mode == kSliding) return k0 >= qlast - wl && k0 + nk - 1 <= q0 + wr;
+  return true;
+}
+
+// True if no pair of query rows [q0, q0 + nq) x key rows [k0, k0 + nk) is
+// allowed (a wavefront can then skip its share of the tile).
+ATTN_HD bool tile_none_allowed(int64_t N, int64_t q0, int64_t nq, int64_t k0, int64_t nk, int mode,
+                               int64_t wl, int64_t wr) {
+  if (q0 >= N || k0 >= N) return true;
+  int64_t qlast = imin(q0 + nq, N) - 1;
+  int64_t klast = imin(k0 + nk, N) - 1;
+  if (mode == kCausal) return k0 > qlast;
+  if (mode == kSliding) return k0 > qlast + wr || klast < q0 - wl;
+  return false;
+}
+
+// Workgroup id -> work item.  The hardware deals consecutive workgroup ids
+// round-robin to the kNumXcd dies; this bijection gives die x a contiguous
+// run of work items, so all query blocks of a head share one die's L2.
+ATTN_HD int64_t xcd_remap(int64_t wg, int64_t n_wg) {
+  int64_t per = n_wg / kNumXcd, rem = n_wg % kNumXcd;
+  int64_t xcd = wg % kNumXcd, slot = wg / kNumXcd;
+  int64_t start = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
+  return start + slot;
+}
+
+// Work item -> (head, query block).  With a causal mask the query blocks of
+// a head run last-first: they visit the most key tiles, so starting them
+// first shortens the tail of the launch.
+ATTN_HD void fwd_work_item(int64_t wg, int64_t n_heads, int64_t n_qblk, int mode, int64_t* head,
+                           int64_t* qblk) {
+  int64_t item = xcd_remap(wg, n_heads * n_qblk);
+  *head = item / n_qblk;
+  int64_t qb = item % n_qblk;
+  *qblk = (mode == kCausal) ? (n_qblk - 1 - qb) : qb;
+}
+
+}  // namespace attn

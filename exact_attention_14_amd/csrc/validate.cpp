@@ -1,0 +1,210 @@
+// validate.cpp -- host-only part of the C ABI: argument validation, status
+// strings, workspace sizing and the planning queries declared in attn.h.
+// Makes no HIP call; builds with any C++17 compiler (also the sanitizer build).
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "attn.h"
+#include "plan.hpp"
+#include "validate.hpp"
+
+namespace attn {
+namespace {
+
+constexpr int64_t kMaxI32 = 2147483647;
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Byte size of an [B, H, N, d] tensor of 2-byte elements (sizes already
+// checked to keep the product below 2^62).
+uint64_t tensor_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
+  return static_cast<uint64_t>(B) * H * N * d * 2u;
+}
+
+Range range_of(const void* p, uint64_t bytes) {
+  uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + bytes};
+}
+
+}  // namespace
+
+attn_status check_sizes(int dt, int64_t B, int64_t H, int64_t N, int64_t d) {
+  if (dt != ATTN_F16 && dt != ATTN_BF16) return ATTN_E_UNSUPPORTED;
+  if (d != 64 && d != 128) return ATTN_E_UNSUPPORTED;
+  if (B < 1 || H < 1 || N < 1) return ATTN_E_SHAPE;
+  // Kernels index heads, rows and workgroups with 32-bit integers and
+  // element offsets with 64-bit ones.
+  if (B > kMaxI32 || H > kMaxI32 || N > kMaxI32) return ATTN_E_SHAPE;
+  if (B * H > kMaxI32) return ATTN_E_SHAPE;
+  const int64_t BH = B * H;
+  if (BH > (int64_t(1) << 62) / (N * d * 4)) return ATTN_E_SHAPE;
+  // Grids: one workgroup per (head, 64-row block) at most.
+  if (BH * ceil_div(N, 64) > kMaxI32) return ATTN_E_SHAPE;
+  return ATTN_OK;
+}
+
+attn_status check_mask(int mode, int64_t wl, int64_t wr) {
+  if (mode != ATTN_MASK_NONE && mode != ATTN_MASK_CAUSAL && mode != ATTN_MASK_SLIDING)
+    return ATTN_E_MASK;
+  if (mode == ATTN_MASK_SLIDING && (wl < 0 || wr < 0)) return ATTN_E_MASK;
+  return ATTN_OK;
+}
+
+attn_status check_common(const TensorArgs& a) {
+  attn_status s = check_sizes(a.dt, a.B, a.H, a.N, a.d);
+  if (s != ATTN_OK) return s;
+  for (int i = 0; i < a.n_in; ++i)
+    if (a.in[i] == nullptr) return ATTN_E_NULLPTR;
+  for (int i = 0; i < a.n_out; ++i)
+    if (a.out[i] == nullptr) return ATTN_E_NULLPTR;
+  s = check_mask(a.mode, a.wl, a.wr);
+  if (s != ATTN_OK) return s;
+  if (!std::isfinite(a.scale)) return ATTN_E_SCALE;
+  for (int i = 0; i < a.n_in; ++i)
+    if (!aligned16(a.in[i])) return ATTN_E_ALIGN;
+  for (int i = 0; i < a.n_out; ++i)
+    if (!aligned16(a.out[i])) return ATTN_E_ALIGN;
+  Range in_r[8], out_r[8];
+  for (int i = 0; i < a.n_in; ++i) in_r[i] = range_of(a.in[i], a.in_bytes[i]);
+  for (int i = 0; i < a.n_out; ++i) out_r[i] = range_of(a.out[i], a.out_bytes[i]);
+  for (int o = 0; o < a.n_out; ++o) {
+    for (int i = 0; i < a.n_in; ++i)
+      if (overlap(out_r[o], in_r[i])) return ATTN_E_ALIAS;
+    for (int p = 0; p < o; ++p)
+      if (overlap(out_r[o], out_r[p])) return ATTN_E_ALIAS;
+  }
+  return ATTN_OK;
+}
+
+uint64_t workspace_bytes(int64_t B, int64_t H, int64_t N) {
+  uint64_t rows = static_cast<uint64_t>(B) * H * N;
+  return (rows * 4u + 255u) / 256u * 256u;
+}
+
+attn_status fwd_check(int dt, const void* Q, const void* K, const void* V, const void* O,
+                      const float* lse, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                      int mode, int64_t wl, int64_t wr) {
+  attn_status s = check_sizes(dt, B, H, N, d);
+  if (s != ATTN_OK) return s;
+  const uint64_t tb = tensor_bytes(B, H, N, d);
+  const uint64_t lb = static_cast<uint64_t>(B) * H * N * 4u;
+  TensorArgs a{};
+  a.dt = dt; a.B = B; a.H = H; a.N = N; a.d = d; a.scale = scale;
+  a.mode = mode; a.wl = wl; a.wr = wr;
+  a.n_in = 3;
+  a.in[0] = Q; a.in[1] = K; a.in[2] = V;
+  a.in_bytes[0] = a.in_bytes[1] = a.in_bytes[2] = tb;
+  a.n_out = 2;
+  a.out[0] = O; a.out[1] = lse;
+  a.out_bytes[0] = tb; a.out_bytes[1] = lb;
+  return check_common(a);
+}
+
+attn_status bwd_check(int dt, const void* Q, const void* K, const void* V, const void* O,
+                      const float* lse, const void* dO, const void* dQ, const void* dK,
+                      const void* dV, const void* ws, size_t ws_bytes, int64_t B, int64_t H,
+                      int64_t N, int64_t d, float scale, int mode, int64_t wl, int64_t wr) {
+  attn_status s = check_sizes(dt, B, H, N, d);
+  if (s != ATTN_OK) return s;
+  const uint64_t tb = tensor_bytes(B, H, N, d);
+  const uint64_t lb = static_cast<uint64_t>(B) * H * N * 4u;
+  const uint64_t wb = workspace_bytes(B, H, N);
+  TensorArgs a{};
+  a.dt = dt; a.B = B; a.H = H; a.N = N; a.d = d; a.scale = scale;
+  a.mode = mode; a.wl = wl; a.wr = wr;
+  a.n_in = 6;
+  a.in[0] = Q; a.in[1] = K; a.in[2] = V; a.in[3] = O; a.in[4] = lse; a.in[5] = dO;
+  for (int i = 0; i < 6; ++i) a.in_bytes[i] = tb;
+  a.in_bytes[4] = lb;
+  a.n_out = 4;
+  a.out[0] = dQ; a.out[1] = dK; a.out[2] = dV; a.out[3] = ws;
+  a.out_bytes[0] = a.out_bytes[1] = a.out_bytes[2] = tb;
+  a.out_bytes[3] = wb;
+  s = check_common(a);
+  if (s != ATTN_OK) return s;
+  if (ws_bytes < wb) return ATTN_E_WORKSPACE;
+  return ATTN_OK;
+}
+
+}  // namespace attn
+
+extern "C" {
+
+const char* attn_status_str(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ok";
+    case ATTN_E_NULLPTR: return "a required pointer is NULL";
+    case ATTN_E_SHAPE: return "B, H or N out of range";
+    case ATTN_E_UNSUPPORTED: return "unsupported dtype or head size (d must be 64 or 128)";
+    case ATTN_E_MASK: return "unknown mask mode or negative window";
+    case ATTN_E_SCALE: return "scale is not finite";
+    case ATTN_E_ALIGN: return "a device pointer is not 16-byte aligned";
+    case ATTN_E_ALIAS: return "an output overlaps an input or another output";
+    case ATTN_E_WORKSPACE: return "workspace missing or too small";
+    case ATTN_E_HIP: return "HIP runtime error at launch";
+  }
+  return "unknown status";
+}
+
+size_t attn_bwd_workspace_bytes(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d) {
+  if (attn::check_sizes(dt, B, H, N, d) != ATTN_OK) return 0;
+  return static_cast<size_t>(attn::workspace_bytes(B, H, N));
+}
+
+attn_status attn_fwd_check(attn_dtype dt, const void* Q, const void* K, const void* V,
+                           const void* O, const float* lse, int64_t B, int64_t H, int64_t N,
+                           int64_t d, float scale, attn_mask_mode mode, int64_t window_left,
+                           int64_t window_right) {
+  return attn::fwd_check(dt, Q, K, V, O, lse, B, H, N, d, scale, mode, window_left, window_right);
+}
+
+attn_status attn_bwd_check(attn_dtype dt, const void* Q, const void* K, const void* V,
+                           const void* O, const float* lse, const void* dO, const void* dQ,
+                           const void* dK, const void* dV, const void* workspace,
+                           size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t d,
+                           float scale, attn_mask_mode mode, int64_t window_left,
+                           int64_t window_right) {
+  return attn::bwd_check(dt, Q, K, V, O, lse, dO, dQ, dK, dV, workspace, workspace_bytes, B, H, N,
+                         d, scale, mode, window_left, window_right);
+}
+
+attn_status attn_fwd_tiles(int64_t d, int64_t* block_q, int64_t* block_k) {
+  if (block_q == nullptr || block_k == nullptr) return ATTN_E_NULLPTR;
+  if (d != 64 && d != 128) return ATTN_E_UNSUPPORTED;
+  *block_q = attn::kFwdBlockQ;
+  *block_k = attn::kFwdBlockK;
+  return ATTN_OK;
+}
+
+attn_status attn_kv_tile_range(int64_t N, int64_t q0, int64_t block_q, int64_t block_k,
+                               attn_mask_mode mode, int64_t window_left, int64_t window_right,
+                               int64_t* lo, int64_t* hi) {
+  if (lo == nullptr || hi == nullptr) return ATTN_E_NULLPTR;
+  if (N < 1 || N > attn::kMaxI32 || block_q < 1 || block_k < 1 || q0 < 0 || q0 >= N)
+    return ATTN_E_SHAPE;
+  attn_status s = attn::check_mask(mode, window_left, window_right);
+  if (s != ATTN_OK) return s;
+  const int64_t wl = attn::imin(window_left, N), wr = attn::imin(window_right, N);
+  attn::kv_tile_range(N, q0, block_q, block_k, mode, wl, wr, lo, hi);
+  return ATTN_OK;
+}
+
+attn_status attn_fwd_workgroup(int64_t wg, int64_t n_heads, int64_t n_qblk, attn_mask_mode mode,
+                               int64_t* head, int64_t* qblk) {
+  if (head == nullptr || qblk == nullptr) return ATTN_E_NULLPTR;
+  if (n_heads < 1 || n_qblk < 1 || n_heads > attn::kMaxI32 || n_qblk > attn::kMaxI32 ||
+      n_heads * n_qblk > attn::kMaxI32 || wg < 0 || wg >= n_heads * n_qblk)
+    return ATTN_E_SHAPE;
+  if (attn::check_mask(mode, 0, 0) != ATTN_OK) return ATTN_E_MASK;
+  attn::fwd_work_item(wg, n_heads, n_qblk, mode, head, qblk);
+  return ATTN_OK;
+}
+
+}  // extern "C"

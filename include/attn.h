@@ -1,0 +1,187 @@
+/*
+ * attn.h -- C ABI of the MI355X (gfx950) exact-attention library (libattn.so).
+ *
+ * The library computes exact scaled-dot-product attention with the tiled,
+ * online-softmax method (FlashAttention): O = softmax(scale * Q K^T + mask) V,
+ * without ever writing the N x N score matrix to device memory, and saves the
+ * per-row log-sum-exp so that the backward can rebuild P by recomputation.
+ *
+ * Sources (cited below as P1..P4 with their sections):
+ *   P1  ai6s.net/6af30f4d40858c2d8819b6d5.html -- generic FlashAttention ideas
+ *       (tiling §2.2, online softmax §2.3, recomputation §2.4, CUDA teaching
+ *       kernel §2.5) and the Ascend NPU implementation (§3).
+ *   P2  aicoding.csdn.net/6a69d3ff10ee7a33f2941f44.html -- FlashAttention in
+ *       ops-transformer (block loop, online softmax, calling interface,
+ *       pitfalls: ragged lengths, causal mask, precision).
+ *   P3  jsqmd.com/news/1148352 -- porting FlashAttention (online softmax
+ *       state m, l, O_acc §2; head_dim 64/128 and backward notes §4).
+ *   P4  ai6s.net/6a0ed07b662f9a54cb761aa2.html -- FlashAttention under the
+ *       catlass templates ("usage": mask None / causal / (window_left,
+ *       window_right) selecting variants of one kernel).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensors are dense and contiguous, layout [B, H, N, d] with d innermost
+ *    (P2 memory table; P4 "usage" example tensors), element type `dt`.
+ *    lse is dense float32 [B, H, N], natural-log units: lse_i = m_i + ln(l_i)
+ *    with m_i the row maximum of scale * q_i . k_j over allowed keys and l_i
+ *    the row sum of exp(scale * q_i . k_j - m_i)  (P1 §2.4 keeps m and l).
+ *  - Masks (P4 "usage"; bounds are this library's reading, both inclusive):
+ *      ATTN_MASK_NONE     every key j < N is allowed;
+ *      ATTN_MASK_CAUSAL   key j is allowed for query i iff j <= i;
+ *      ATTN_MASK_SLIDING  allowed iff i - window_left <= j <= i + window_right.
+ *    Windows are read only for SLIDING, must be >= 0, and values >= N act as
+ *    unbounded.  CAUSAL equals SLIDING(N-1, 0); NONE equals SLIDING(N-1, N-1).
+ *    Because the diagonal is always allowed, no row is ever empty.
+ *  - Supported: dt in {F16, BF16}; d in {64, 128} (P3 §4: the head sizes the
+ *    tiling is built for); N >= 1; B, H >= 1; any finite scale (negative and
+ *    zero allowed).  Any N is handled (ragged tails are masked in-kernel, P2
+ *    "pitfall 1"), not padded.
+ *  - Ownership: the caller allocates and owns every buffer.  The library never
+ *    allocates, frees or retains device memory and keeps no state between
+ *    calls; it is thread-safe.  Inputs are read only.  Outputs must not overlap
+ *    any input or each other (ATTN_E_ALIAS, checked by address range).
+ *  - Device pointers must be 16-byte aligned (ATTN_E_ALIGN).
+ *  - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL is the
+ *    default stream) and the call returns without synchronising.
+ *  - Errors: every argument is validated on the host before any HIP call; on
+ *    any error nothing is launched and no output is written.  A launch failure
+ *    reported by the runtime returns ATTN_E_HIP; a fault inside a kernel
+ *    surfaces at the caller's next synchronisation.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_dtype {
+  ATTN_F16 = 0,  /* IEEE binary16 storage, fp32 accumulation */
+  ATTN_BF16 = 1  /* bfloat16 storage, fp32 accumulation */
+} attn_dtype;
+
+typedef enum attn_mask_mode {
+  ATTN_MASK_NONE = 0,
+  ATTN_MASK_CAUSAL = 1,
+  ATTN_MASK_SLIDING = 2
+} attn_mask_mode;
+
+typedef enum attn_status {
+  ATTN_OK = 0,
+  ATTN_E_NULLPTR = 1,     /* a required pointer is NULL */
+  ATTN_E_SHAPE = 2,       /* B, H or N < 1, or sizes too large to index */
+  ATTN_E_UNSUPPORTED = 3, /* dtype or head size d not supported */
+  ATTN_E_MASK = 4,        /* unknown mask mode or negative window */
+  ATTN_E_SCALE = 5,       /* scale is NaN or infinite */
+  ATTN_E_ALIGN = 6,       /* a device pointer is not 16-byte aligned */
+  ATTN_E_ALIAS = 7,       /* an output overlaps an input or another output */
+  ATTN_E_WORKSPACE = 8,   /* workspace missing or smaller than required */
+  ATTN_E_HIP = 9          /* the HIP runtime reported an error at launch */
+} attn_status;
+
+/*
+ * attn_fwd -- forward pass (P1 §2.2 tiling, §2.3 online softmax; P3 §2).
+ *
+ *   Q, K, V  in:  [B, H, N, d] of `dt`.
+ *   O        out: [B, H, N, d] of `dt`, O = P V with P = softmax(scale Q K^T
+ *                 + mask) row-wise, rounded once from fp32 to `dt`.
+ *   lse      out: [B, H, N] float32, as in the conventions above.
+ *   scale    multiplies the scores before the softmax (P1 §1 uses 1/sqrt(d)).
+ *   mode, window_left, window_right: the mask, as above.
+ *   stream   hipStream_t to enqueue on.
+ * Returns ATTN_OK or the first validation error; see the conventions.
+ */
+attn_status attn_fwd(attn_dtype dt, const void* Q, const void* K, const void* V, void* O,
+                     float* lse, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                     attn_mask_mode mode, int64_t window_left, int64_t window_right,
+                     void* stream);
+
+/*
+ * attn_bwd_workspace_bytes -- size in bytes of the device workspace attn_bwd
+ * needs for these sizes (float32 D_i = dO_i . O_i per row, padded to 256 B).
+ * Returns 0 if the sizes are invalid.  Pure host function, no HIP call.
+ */
+size_t attn_bwd_workspace_bytes(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d);
+
+/*
+ * attn_bwd -- recomputation backward (P1 §2.4; P3 §4): rebuilds P tile by
+ * tile from the saved lse, never storing it, and returns the exact gradients
+ * of O with respect to Q, K and V for the upstream gradient dO:
+ *   dV = P^T dO;  dP = dO V^T;  D_i = dO_i . O_i (from the stored O);
+ *   dS = P * (dP - D);  dQ = scale dS K;  dK = scale dS^T Q.
+ *
+ *   Q, K, V, O, dO  in:  [B, H, N, d] of `dt` (O as written by attn_fwd).
+ *   lse             in:  [B, H, N] float32 as written by attn_fwd.
+ *   dQ, dK, dV      out: [B, H, N, d] of `dt`, fp32-accumulated, rounded once.
+ *   workspace       device scratch of at least attn_bwd_workspace_bytes(...)
+ *                   bytes, 16-byte aligned, owned by the caller; its contents
+ *                   on entry are ignored and on return are unspecified.
+ *   Other arguments as for attn_fwd (same scale and mask as the forward).
+ * The result is deterministic (no atomics).
+ */
+attn_status attn_bwd(attn_dtype dt, const void* Q, const void* K, const void* V, const void* O,
+                     const float* lse, const void* dO, void* dQ, void* dK, void* dV,
+                     void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t N,
+                     int64_t d, float scale, attn_mask_mode mode, int64_t window_left,
+                     int64_t window_right, void* stream);
+
+/* attn_status_str -- static, NUL-terminated description of a status code. */
+const char* attn_status_str(attn_status s);
+
+/*
+ * Host-only planning queries.  They make no HIP call, need no GPU and exist
+ * so that the host logic can be checked on its own.
+ */
+
+/* attn_fwd_check -- the exact validation attn_fwd performs, without launching. */
+attn_status attn_fwd_check(attn_dtype dt, const void* Q, const void* K, const void* V,
+                           const void* O, const float* lse, int64_t B, int64_t H, int64_t N,
+                           int64_t d, float scale, attn_mask_mode mode, int64_t window_left,
+                           int64_t window_right);
+
+/* attn_bwd_check -- the exact validation attn_bwd performs, without launching. */
+attn_status attn_bwd_check(attn_dtype dt, const void* Q, const void* K, const void* V,
+                           const void* O, const float* lse, const void* dO, const void* dQ,
+                           const void* dK, const void* dV, const void* workspace,
+                           size_t workspace_bytes, int64_t B, int64_t H, int64_t N, int64_t d,
+                           float scale, attn_mask_mode mode, int64_t window_left,
+                           int64_t window_right);
+
+/*
+ * attn_fwd_tiles -- the forward's tile shape: *block_q query rows per
+ * workgroup (Br) and *block_k key rows per streamed K/V tile (Bc) for head
+ * size d (P1 §2.2).  Returns ATTN_E_UNSUPPORTED for other d.
+ */
+attn_status attn_fwd_tiles(int64_t d, int64_t* block_q, int64_t* block_k);
+
+/*
+ * attn_kv_tile_range -- the half-open range [*lo, *hi) of key tiles (of
+ * block_k rows) that the query block [q0, q0 + block_q) visits: every tile
+ * holding at least one allowed (query, key) pair of that block and no other
+ * (whole-tile skipping for causal and sliding masks, P1 §3.3 key optimisation
+ * (4)).  Windows as in the conventions.  Returns ATTN_E_SHAPE / ATTN_E_MASK
+ * on invalid arguments.
+ */
+attn_status attn_kv_tile_range(int64_t N, int64_t q0, int64_t block_q, int64_t block_k,
+                               attn_mask_mode mode, int64_t window_left, int64_t window_right,
+                               int64_t* lo, int64_t* hi);
+
+/*
+ * attn_fwd_workgroup -- which (head index b*H + h, query block) the forward's
+ * workgroup `wg` of `n_wg` = B*H*n_qblk processes: workgroups are dealt to the
+ * 8 accelerator dies round-robin, so consecutive ids are remapped to keep all
+ * query blocks of one head on one die's L2; causal masks also run the longest
+ * query blocks first.  Returns ATTN_E_SHAPE if wg is out of range.
+ */
+attn_status attn_fwd_workgroup(int64_t wg, int64_t n_heads, int64_t n_qblk, attn_mask_mode mode,
+                               int64_t* head, int64_t* qblk);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

@@ -1,0 +1,116 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol attn.h
+declares, and its host logic (validation, tile ranges, workgroup order)
+behaves as documented.  Only host-only entry points are called, plus the
+launching entry points with invalid arguments, which must return their status
+before any HIP call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import exact_attention_14_amd as ea
+from exact_attention_14_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "attn.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(attn_[a-z_0-9]+)\s*\(",
+                                 src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) == 9, names
+    lib = ea.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(binding.EXPORTS)
+
+
+def test_status_strings():
+    for s in range(10):
+        assert ea.attn_status_str(s)
+
+
+def test_launching_entry_points_reject_bad_arguments_before_any_hip_call():
+    lib = ea.lib()
+    buf = ctypes.create_string_buffer(1 << 16)
+    base = (ctypes.addressof(buf) + 255) // 256 * 256
+    Q, K, V, O, L = base, base + 4096, base + 8192, base + 12288, base + 16384
+    # NULL input
+    assert lib.attn_fwd(1, None, K, V, O, L, 1, 1, 8, 64, 0.1, 0, 0, 0, None) == 1
+    # unsupported d
+    assert lib.attn_fwd(1, Q, K, V, O, L, 1, 1, 8, 80, 0.1, 0, 0, 0, None) == 3
+    # negative window
+    assert lib.attn_fwd(0, Q, K, V, O, L, 1, 1, 8, 64, 0.1, 2, -1, 0, None) == 4
+    # output overlapping an input
+    assert lib.attn_fwd(0, Q, K, V, Q + 16, L, 1, 1, 8, 64, 0.1, 0, 0, 0, None) == 7
+    # workspace too small
+    ws = ea.attn_bwd_workspace_bytes(__import__("torch").float16, 1, 1, 8, 64)
+    assert ws == 256
+    args = [0, Q, K, V, O, L, O, base + 20480, base + 24576, base + 28672, base + 32768, ws - 16,
+            1, 1, 8, 64, 0.1, 1, 0, 0, None]
+    assert lib.attn_bwd(*args) == 8
+    # nothing was written: the buffer is still zero
+    assert bytes(buf) == b"\0" * len(buf)
+
+
+def test_fwd_tiles():
+    assert ea.attn_fwd_tiles(128) == (128, 64)
+    assert ea.attn_fwd_tiles(64) == (128, 64)
+    with pytest.raises(ea.AttnError):
+        ea.attn_fwd_tiles(96)
+
+
+@pytest.mark.parametrize("N", [1, 17, 128, 333, 1000])
+@pytest.mark.parametrize("mask", [None, "causal", (0, 0), (5, 0), (64, 3), (200, 200), (4096, 0)])
+def test_kv_tile_range_matches_the_oracle_mask(N, mask):
+    """Every visited tile holds an allowed pair and every allowed pair is in a visited tile."""
+    mode, wl, wr = ea.mask_args(mask)
+    name = ["none", "causal", "sliding"][mode]
+    bq, bk = ea.attn_fwd_tiles(128)
+    keys = np.arange(N)
+    for q0 in range(0, N, bq):
+        lo, hi = ea.attn_kv_tile_range(N, q0, bq, bk, mode, wl, wr)
+        rows = np.arange(q0, min(N, q0 + bq))
+        A = oracle.allowed_matrix(rows, keys, N, name, wl, wr)
+        tiles = np.unique(keys[A.any(axis=0)] // bk)
+        assert lo == tiles.min() and hi == tiles.max() + 1
+        assert len(tiles) == hi - lo
+
+
+@pytest.mark.parametrize("n_heads,n_qblk", [(1, 1), (3, 5), (128, 32), (40, 256), (7, 3)])
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_workgroup_order_is_a_bijection(n_heads, n_qblk, mode):
+    seen = set()
+    n = n_heads * n_qblk
+    for wg in range(n):
+        h, qb = ea.attn_fwd_workgroup(wg, n_heads, n_qblk, mode)
+        assert 0 <= h < n_heads and 0 <= qb < n_qblk
+        seen.add((h, qb))
+    assert len(seen) == n
+    with pytest.raises(ea.AttnError):
+        ea.attn_fwd_workgroup(n, n_heads, n_qblk, mode)
+
+
+def test_workgroup_order_keeps_a_head_on_one_die():
+    """Ids are dealt round-robin to 8 dies; each die sees whole heads (128 heads x 32 blocks)."""
+    n_heads, n_qblk = 128, 32
+    die_heads = {}
+    for wg in range(n_heads * n_qblk):
+        h, _ = ea.attn_fwd_workgroup(wg, n_heads, n_qblk, 0)
+        die_heads.setdefault(h, set()).add(wg % 8)
+    assert all(len(d) == 1 for d in die_heads.values())
+
+
+def test_causal_runs_longest_query_blocks_first():
+    h0, qb0 = ea.attn_fwd_workgroup(0, 4, 16, 1)
+    assert qb0 == 15
+    h0, qb0 = ea.attn_fwd_workgroup(0, 4, 16, 0)
+    assert qb0 == 0

@@ -1,0 +1,79 @@
+"""GPU parity of the recomputation backward against the fp64 oracle.
+
+dQ, dK, dV within relative Frobenius error 1e-2 per tensor on small and ragged
+shapes with every mask; invariants of the exact gradient on the GPU's output.
+"""
+import pytest
+import torch
+
+import exact_attention_14_amd as ea
+from parity_util import bwd_case, gpu, say
+from workloads import draw
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("N", [2, 17, 64, 65, 129, 300])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_backward_ragged(N, d, dtype):
+    # With only one or two allowed keys per row, dP - D nearly cancels and the
+    # rounding of O to bf16 (D is formed from the stored O) dominates dS: the
+    # same roundings applied in fp64 give 6.6e-2 for N = 2 causal.  That case
+    # gets a 1e-1 bar; every other case keeps 1e-2.
+    tol = 1e-1 if (dtype == "bf16" and N < 16) else 1e-2
+    for mask in [None, "causal", (9, 4)]:
+        say(f"bwd N={N} d={d} {dtype} mask={mask}")
+        bwd_case(1, 2, N, d, dtype, mask, seed=N + d, tol=tol)
+
+
+@pytest.mark.parametrize("mask", [None, "causal", (1, 0), (100, 0), (63, 65), (2000, 2000)])
+def test_backward_masks_multi_tile(mask):
+    say(f"bwd N=1000 mask={mask}")
+    bwd_case(2, 2, 1000, 128, "f16", mask, seed=3)
+
+
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 0.9])
+def test_backward_scales(scale):
+    say(f"bwd scale={scale}")
+    bwd_case(1, 2, 200, 64, "bf16", "causal", seed=4, scale=scale)
+
+
+@pytest.mark.parametrize("N,mask", [(1, None), (1, "causal"), (300, (0, 0))])
+def test_backward_single_allowed_key(N, mask):
+    """Every row has one allowed key: P = I, so dV = dO and the exact dQ = dK = 0.
+
+    A relative error is undefined for a zero reference; the GPU's dQ and dK
+    (rounding of dP - D, computed in two summation orders) must be tiny
+    against the gradient's natural size ||dO||.
+    """
+    inp = draw(1, 2, N, 128, "bf16", 22, with_do=True)
+    q, k, v, do = (gpu(inp[x]) for x in ("q", "k", "v", "do"))
+    o, lse = ea.attn_fwd(q, k, v, mask=mask)
+    dq, dk, dv = ea.attn_bwd(q, k, v, o, lse, do, mask=mask)
+    torch.cuda.synchronize()
+    assert torch.equal(o, v)
+    assert torch.equal(dv, do)
+    ref = do.float().norm().item()
+    say(f"single-key N={N}: |dQ| {dq.float().norm().item():.3e} |dK| {dk.float().norm().item():.3e} "
+        f"|dO| {ref:.3e}")
+    assert dq.float().norm().item() <= 1e-4 * ref
+    assert dk.float().norm().item() <= 1e-4 * ref
+
+
+def test_backward_invariants_and_determinism():
+    N = 1500
+    inp = draw(1, 4, N, 128, "f16", 21, with_do=True)
+    q, k, v, do = (gpu(inp[x]) for x in ("q", "k", "v", "do"))
+    for mask in [None, "causal", (200, 0)]:
+        o, lse = ea.attn_fwd(q, k, v, mask=mask)
+        dq, dk, dv = ea.attn_bwd(q, k, v, o, lse, do, mask=mask)
+        dq2, dk2, dv2 = ea.attn_bwd(q, k, v, o, lse, do, mask=mask)
+        assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+        dks = dk.float().sum(dim=2).norm(dim=2)
+        assert torch.all(dks <= 1e-2 * dk.float().norm(dim=(2, 3)))
+        diff = (dv.float().sum(dim=2) - do.float().sum(dim=2)).norm(dim=2)
+        assert torch.all(diff <= 1e-2 * do.float().sum(dim=2).norm(dim=2))
+        z = ea.attn_bwd(q, k, v, o, lse, torch.zeros_like(do), mask=mask)
+        for g in z:
+            assert torch.count_nonzero(g).item() == 0
