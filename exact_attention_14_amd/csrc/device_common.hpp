@@ -100,6 +100,83 @@ __device__ __forceinline__ float halves_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// v *= s elementwise, in place.  Written with a tied operand so that a
+// rarely-taken rescale keeps the accumulator in the registers it already
+// occupies (otherwise the common path pays a copy of every register to merge
+// the two versions).
+__device__ __forceinline__ void scale_in_place(f32x16_t& v, float s) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float x = v[i];
+    asm volatile("v_mul_f32 %0, %0, %1" : "+v"(x) : "v"(s));
+    v[i] = x;
+  }
+}
+
+// Buffer resources over one head's rows: loads past `bytes` return zeros and
+// stores past it are dropped by the hardware, which is how ragged tails and
+// padding rows are handled without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                              uint32_t soff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                         r, static_cast<int>(voff), static_cast<int>(soff), 0));
+}
+__device__ __forceinline__ void buf_store8(u32x2_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), r,
+                                        static_cast<int>(voff), 0, 0);
+}
+__device__ __forceinline__ void buf_store4(float v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, static_cast<int>(voff), 0, 0);
+}
+
+// Direct HBM-to-LDS load of 16 bytes per lane: lane i of the wavefront writes
+// lds + 16*i (the LDS address is wavefront-uniform); past `bytes` of the
+// buffer the hardware writes zeros.
+__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t voff,
+                                               uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds), 16,
+                                           static_cast<int>(voff), static_cast<int>(soff), 0, 0);
+}
+
+// Waits until every vector-memory operation this wavefront issued (including
+// direct-to-LDS loads) has completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Scheduling-group masks for __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedValu = 0x002;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
+
+// Asks the scheduler for a software-pipelined order: PRE groups of `reads`
+// LDS reads up front, then N times {one matrix instruction, `valu` vector-ALU
+// instructions, `reads` LDS reads for a later matrix instruction}, so that
+// LDS latency and independent vector work both hide behind the matrix core.
+template <int N, int READS, int VALU, int PRE>
+__device__ __forceinline__ void interleave_mfma() {
+  if (PRE * READS > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PRE * READS, 0);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    if (VALU > 0) __builtin_amdgcn_sched_group_barrier(kSchedValu, VALU, 0);
+    if (READS > 0 && i + PRE < N) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, READS, 0);
+  }
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lanes 4t .. 4t+3 point at the four 4-element pieces of row t of a 4 x 16
+// block of 16-bit elements; lane j of the group receives column j, i.e. the
+// four elements (row 0..3, column j).
+__device__ __forceinline__ u32x2_t ld_lds_tr8(const char* p) {
+  typedef short s16x4_t __attribute__((ext_vector_type(4)));
+  return __builtin_bit_cast(
+      u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                   (__attribute__((address_space(3))) s16x4_t*)(p)));
+}
+
 // Transpose helper: from four 32-bit words holding element pairs (e, e+1) of
 // four rows r0..r3, build two words per element: (r0, r1) and (r2, r3).
 // byte selectors for v_perm_b32 (bytes 0..3 of the second operand, 4..7 of

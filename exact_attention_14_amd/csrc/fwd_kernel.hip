@@ -6,9 +6,10 @@
 //
 // * One workgroup = 4 wavefronts = 128 query rows of one head; each wavefront
 //   owns 32 query rows for the whole launch.  K/V are streamed in 64-row
-//   tiles through a two-stage LDS ring (P1 §3.2 double-buffered queues): tile
-//   t+1 is fetched from HBM into registers while tile t is consumed, then
-//   written to the other stage.
+//   tiles through two-stage LDS rings (P1 §3.2 double-buffered queues),
+//   loaded by direct HBM-to-LDS buffer loads that need no registers.  Loads
+//   and stores go through buffer resources bounded by the head's size, so
+//   rows past N read as zeros and stores past N are dropped without branches.
 // * Scores are computed transposed, S^T = K Q^T, on the 32x32x16 matrix
 //   cores: K (A operand) comes from LDS, Q (B operand) stays in registers for
 //   the whole launch.  In the result tile each lane owns one query row and 16
@@ -16,9 +17,16 @@
 //   two halves of the wavefront (P3 §4: warp shuffles must be rewritten for
 //   non-NVIDIA GPUs; here v_permlane32_swap).
 // * The output is accumulated transposed too, O^T += V^T P^T: the score tile
-//   converted to 16-bit is already the B operand, V^T (A operand) is stored
-//   transposed in LDS in the matching permuted key order, and the per-row
-//   rescale factor of the online softmax applies to the lane's own column.
+//   converted to 16-bit is already the B operand, and V^T (A operand) is read
+//   from row-major V in LDS with the transposing ds_read_b64_tr_b16, in the
+//   key order the score tile's layout implies.  The per-row rescale factor of
+//   the online softmax applies to the lane's own column.
+// * LDS layouts: K rows are padded by 16 bytes so that 16 lanes reading the
+//   same 16-byte chunk of 16 consecutive rows hit distinct banks; V rows keep
+//   their natural pitch with 16-byte chunks XOR-swizzled by (row mod 4) so
+//   that the eight rows one transposing read touches spread over all banks.
+//   The loop is unrolled over the two stages, so every LDS address is a
+//   per-lane constant plus an immediate offset.
 // * Scores go straight to the exp2 domain with one FMA, s*c - m, where
 //   c = |scale| * log2(e) (P1 §2.5 and §3.3 (2): exp2 instead of exp).  A
 //   negative scale is folded into Q by flipping its sign bits (exact).
@@ -41,6 +49,8 @@
 //   row up to the final rounding; lse = (m + log2 l) * ln 2.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernels.hpp"
 #include "plan.hpp"
@@ -50,34 +60,55 @@ namespace {
 
 constexpr float kTau = 8.0f;
 
+template <int D>
+struct FwdLayout {
+  static constexpr int BC = kFwdBlockK;
+  static constexpr int NCH = D / 8;                  // 16-byte chunks per row
+  static constexpr int K_PITCH = D * 2 + 16;         // padded K row
+  static constexpr int V_PITCH = D * 2;
+  static constexpr int K_BYTES = BC * K_PITCH;
+  static constexpr int V_BYTES = BC * V_PITCH;
+  // Two K stages then two V stages.
+  static constexpr int K_STAGE0 = 0, K_STAGE1 = K_BYTES;
+  static constexpr int V_STAGE0 = 2 * K_BYTES, V_STAGE1 = 2 * K_BYTES + V_BYTES;
+  static constexpr int LDS_BYTES = 2 * K_BYTES + 2 * V_BYTES;
+  // K and V go straight to LDS: each wavefront instruction fills 1 KiB.  K
+  // rows have NCH + 1 slots of 16 bytes (the last one is padding).
+  static constexpr int K_SLOTS = BC * (NCH + 1);
+  static constexpr int K_INSTR = K_SLOTS / 64;                 // 17 at d = 128, 9 at d = 64
+  static constexpr int K_INSTR_PER_WAVE = (K_INSTR + 3) / 4;   // waves take j = w, w+4, ...
+  static constexpr int V_WAVE_LOADS = V_BYTES / (kFwdThreads / 64) / 1024;
+  static constexpr int V_ROWS_PER_1K = 1024 / (D * 2);
+  static constexpr int VSWZ_MASK = NCH / 4 - 1;             // row bits used by the V swizzle
+  static __device__ __forceinline__ int vswz(int row) { return (row & VSWZ_MASK) << 2; }
+  static __host__ __device__ constexpr int kstage(int s) { return s ? K_STAGE1 : K_STAGE0; }
+  static __host__ __device__ constexpr int vstage(int s) { return s ? V_STAGE1 : V_STAGE0; }
+};
+
 template <typename T, int D, int MASK>
 __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(FwdParams p) {
+  using L = FwdLayout<D>;
   constexpr int BR = kFwdBlockQ, BC = kFwdBlockK;
-  constexpr int NCH = D / 8;               // 16-byte chunks per row
   constexpr int KSTEPS = D / 16;           // reduction steps over d
   constexpr int DBLK = D / 32;             // 32-row blocks of O^T
-  constexpr int KSWZ = NCH < 16 ? NCH : 16;
-  constexpr int K_BYTES = BC * D * 2;
-  constexpr int VT_PITCH = BC * 2;         // bytes per V^T row (one d index)
-  constexpr int STAGE_BYTES = 2 * K_BYTES;
-  constexpr int K_PER_THREAD = BC * NCH / kFwdThreads;
-  static_assert(K_PER_THREAD >= 1, "K tile loader");
-  static_assert((BC / 4) * NCH <= kFwdThreads, "V tile loader");
+  constexpr uint32_t ROW_BYTES = D * 2;
 
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, r32 = lane & 31;
+  const int lane = tid & 63, half = lane >> 5, r32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wavefront
   const int N = p.N;
 
   int64_t head, qblk;
   fwd_work_item(blockIdx.x, p.n_heads, p.n_qblk, MASK, &head, &qblk);
   const int q0 = static_cast<int>(qblk) * BR;
-  const size_t hoff = static_cast<size_t>(head) * N * D;
-  const char* Qh = reinterpret_cast<const char*>(p.Q) + hoff * 2;
-  const char* Kh = reinterpret_cast<const char*>(p.K) + hoff * 2;
-  const char* Vh = reinterpret_cast<const char*>(p.V) + hoff * 2;
+  const size_t hoff = static_cast<size_t>(head) * N * D * 2;
+  const uint32_t head_bytes = static_cast<uint32_t>(N) * ROW_BYTES;
+  const auto rQ = make_rsrc(reinterpret_cast<const char*>(p.Q) + hoff, head_bytes);
+  const auto rK = make_rsrc(reinterpret_cast<const char*>(p.K) + hoff, head_bytes);
+  const auto rV = make_rsrc(reinterpret_cast<const char*>(p.V) + hoff, head_bytes);
 
   int64_t lo64, hi64;
   kv_tile_range(N, q0, BR, BC, MASK, p.wl, p.wr, &lo64, &hi64);
@@ -88,14 +119,9 @@ void fwd_kernel(FwdParams p) {
   const int qrow = wq0 + r32;
   u32x4_t qf[KSTEPS];
 #pragma unroll
-  for (int ks = 0; ks < KSTEPS; ++ks) {
-    if (qrow < N) {
-      qf[ks] = ld_global16(Qh + (static_cast<size_t>(qrow) * D + ks * 16 + half * 8) * 2);
-      qf[ks] ^= p.qsign;
-    } else {
-      qf[ks] = u32x4_t{0, 0, 0, 0};
-    }
-  }
+  for (int ks = 0; ks < KSTEPS; ++ks)
+    qf[ks] = buf_load16(rQ, static_cast<uint32_t>(qrow) * ROW_BYTES + ks * 32 + half * 16, 0) ^
+             p.qsign;
 
   f32x16_t acc[DBLK];
 #pragma unroll
@@ -103,175 +129,209 @@ void fwd_kernel(FwdParams p) {
   float m = -INFINITY, l = 0.0f, lr = 0.0f;
   const float c = p.c;
 
-  // Loader assignment.  K: thread owns chunks (row, ch) = divmod(tid + 256 j,
-  // NCH).  V: thread owns 4 consecutive rows of one chunk, if tid < 16*NCH.
-  u32x4_t kst[K_PER_THREAD];
-  u32x4_t vst[4];
-  const bool v_loader = tid < (BC / 4) * NCH;
-  const int v_rg = tid / NCH, v_ch = tid % NCH;
+  static_assert(L::K_SLOTS % 64 == 0, "K tile must fill whole 1 KiB loads");
+  // K direct loads: instruction j (= wave + 4i) fills 16-byte slots
+  // s = 64j + lane of the stage; slot s holds row s / (NCH+1), chunk
+  // s % (NCH+1).  Padding slots point past the end of the head, so the
+  // hardware fills them with zeros without touching memory.
+  uint32_t kg_off[L::K_INSTR_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < L::K_INSTR_PER_WAVE; ++i) {
+    const int slot = (wave + 4 * i) * 64 + lane;
+    const int row = slot / (L::NCH + 1), ch = slot % (L::NCH + 1);
+    kg_off[i] = ch == L::NCH ? head_bytes : static_cast<uint32_t>(row) * ROW_BYTES + ch * 16;
+  }
+  // V direct loads: instruction j of wavefront w fills LDS bytes
+  // [(4j + w) KiB, +1 KiB) of the stage, i.e. 16-byte slot s = 64*(4j+w) + lane
+  // = (row, physical chunk); the lane fetches the logical chunk stored there.
+  const int vs_slot = wave * 64 + lane;
+  const int vs_row = vs_slot / L::NCH, vs_phys = vs_slot % L::NCH;
+  const uint32_t vg_off = static_cast<uint32_t>(vs_row) * ROW_BYTES +
+                          ((vs_phys ^ L::vswz(vs_row)) << 4);
 
-  auto gload = [&](int t) {
-    const int k0 = t * BC;
+  // Readers.  K (A of S^T): row kb*32 + r32, chunk 2kk + half.
+  const int kr_off = r32 * L::K_PITCH + half * 16;
+  // V^T (A of O^T) via transposing reads: lane (group G = lane/16, t, cc) of
+  // the 16-lane group points at row 16ks + 4*half + t (+8 for the second
+  // read), columns 32db + 16*(G%2) + 4cc .. +3.
+  const int G = lane >> 4, tt = (lane >> 2) & 3, cc = lane & 3;
+  int vr_off[DBLK];
 #pragma unroll
-    for (int j = 0; j < K_PER_THREAD; ++j) {
-      const int item = tid + kFwdThreads * j;
-      const int key = k0 + item / NCH, ch = item % NCH;
-      kst[j] = key < N ? ld_global16(Kh + (static_cast<size_t>(key) * D + ch * 8) * 2)
-                       : u32x4_t{0, 0, 0, 0};
-    }
-    if (v_loader) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = k0 + v_rg * 4 + r;
-        vst[r] = key < N ? ld_global16(Vh + (static_cast<size_t>(key) * D + v_ch * 8) * 2)
-                         : u32x4_t{0, 0, 0, 0};
-      }
-    }
-  };
+  for (int db = 0; db < DBLK; ++db) {
+    const int row = 4 * half + tt;
+    const int chunk = 4 * db + 2 * (G & 1) + (cc >> 1);
+    vr_off[db] = row * L::V_PITCH + ((chunk ^ L::vswz(row)) << 4) + (cc & 1) * 8;
+  }
 
-  auto swrite = [&](int stage) {
-    char* ks = smem + stage * STAGE_BYTES;
-    char* vs = ks + K_BYTES;
+  auto gload_k_lds = [&](int t, int off) {
+    const uint32_t soff = static_cast<uint32_t>(t * BC) * ROW_BYTES;
 #pragma unroll
-    for (int j = 0; j < K_PER_THREAD; ++j) {
-      const int item = tid + kFwdThreads * j;
-      const int row = item / NCH, ch = item % NCH;
-      st_lds16(ks + (row * NCH + (ch ^ (row & (KSWZ - 1)))) * 16, kst[j]);
-    }
-    if (v_loader) {
-      // V^T row = d index; keys stored at perm16 positions, 16-byte chunks
-      // XOR-swizzled by the row index.
-      const int pos = perm16(v_rg * 4);  // 4 consecutive keys stay adjacent
-      const int chunk = pos >> 3, sub = (pos & 7) * 2;
-      write_transposed_4x8(vs, vst, v_ch * 8, [&](int drow) {
-        return drow * VT_PITCH + ((chunk ^ (drow & 7)) << 4) + sub;
-      });
+    for (int i = 0; i < L::K_INSTR_PER_WAVE; ++i) {
+      const int j = wave + 4 * i;
+      if (j < L::K_INSTR) buf_load16_lds(rK, smem + off + j * 1024, kg_off[i], soff);
     }
   };
-
-  gload(lo);
-  swrite(0);
-  __syncthreads();
-
-  for (int t = lo; t < hi; ++t) {
-    const int stage = (t - lo) & 1;
-    const bool more = t + 1 < hi;
-    if (more) gload(t + 1);
-    const char* ks = smem + stage * STAGE_BYTES;
-    const char* vs = ks + K_BYTES;
-    const int k0 = t * BC;
-
-    if (!tile_none_allowed(N, wq0, 32, k0, BC, MASK, p.wl, p.wr)) {
-      // S^T = K Q^T for two 32-key blocks.
-      f32x16_t s[2];
+  auto gload_v_lds = [&](int t, int off) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16_t{};
-        const int row = kb * 32 + r32;
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-          const int ch = kk * 2 + half;
-          const u32x4_t a = ld_lds16(ks + (row * NCH + (ch ^ (row & (KSWZ - 1)))) * 16);
-          s[kb] = Elem<T>::mma(a, qf[kk], s[kb]);
-        }
-      }
+    for (int j = 0; j < L::V_WAVE_LOADS; ++j)
+      buf_load16_lds(rV, smem + off + (4 * j + wave) * 1024, vg_off,
+                     static_cast<uint32_t>(t * BC + 4 * j * L::V_ROWS_PER_1K) * ROW_BYTES);
+  };
 
-      if (!tile_all_allowed(N, wq0, 32, k0, BC, MASK, p.wl, p.wr)) {
+  // S^T = K Q^T of tile t from a K stage: two independent accumulation chains.
+  auto scores = [&](int koff, f32x16_t s[2]) {
+    s[0] = f32x16_t{};
+    s[1] = f32x16_t{};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-            bool ok = key < N;
-            if (MASK == kCausal) ok = ok && key <= qrow;
-            if (MASK == kSliding) ok = ok && key >= qrow - p.wl && key <= qrow + p.wr;
-            if (!ok) s[kb][i] = -INFINITY;
-          }
-        }
-      }
-
-      // Online softmax update (exp2 domain).
-      float mx = -INFINITY;
+    for (int kk = 0; kk < KSTEPS; ++kk)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-      mx = halves_max(mx);
-      const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
-      const float mnew = fmaxf(m, mt);
-      const bool resc = mnew > m + kTau;
-      float corr = 1.0f;
-      if (resc) {
-        corr = fast_exp2(m - mnew);
-        m = mnew;
-      }
-      if (__any(resc)) {
-#pragma unroll
-        for (int b = 0; b < DBLK; ++b) acc[b] *= corr;
-        l *= corr;
-        lr *= corr;
-      }
-      const float base = (m == -INFINITY) ? 0.0f : m;
+        s[kb] = Elem<T>::mma(ld_lds16(smem + koff + kr_off + kb * 32 * L::K_PITCH + kk * 32),
+                             qf[kk], s[kb]);
+  };
 
-      uint32_t pk[2][8];
-      float rs[2] = {0.0f, 0.0f}, rr[2] = {0.0f, 0.0f};
+  // Phase 1 of tile t: mask (boundary tiles only), row max, and the online
+  // rescale (rare).  Returns the exponent base.
+  auto softmax_max = [&](int t, f32x16_t s[2]) {
+    const int k0 = t * BC;
+    if (!tile_all_allowed(N, wq0, 32, k0, BC, MASK, p.wl, p.wr)) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float e0 = fast_exp2(fmaf(s[kb][2 * j], c, -base));
-          const float e1 = fast_exp2(fmaf(s[kb][2 * j + 1], c, -base));
-          rs[kb] += e0 + e1;
-          pk[kb][j] = Elem<T>::pack2(e0, e1);
-          rr[kb] = Elem<T>::add_pair(pk[kb][j], rr[kb]);
-        }
-      }
-      l += rs[0] + rs[1];
-      lr += rr[0] + rr[1];
-
-      // O^T += V^T P^T over four 16-key steps.
-#pragma unroll
-      for (int kk = 0; kk < BC / 16; ++kk) {
-        const u32x4_t b = {pk[kk >> 1][(kk & 1) * 4 + 0], pk[kk >> 1][(kk & 1) * 4 + 1],
-                           pk[kk >> 1][(kk & 1) * 4 + 2], pk[kk >> 1][(kk & 1) * 4 + 3]};
-        const int chunk = kk * 2 + half;
-#pragma unroll
-        for (int db = 0; db < DBLK; ++db) {
-          const int drow = db * 32 + r32;
-          const u32x4_t a = ld_lds16(vs + drow * VT_PITCH + ((chunk ^ (drow & 7)) << 4));
-          acc[db] = Elem<T>::mma(a, b, acc[db]);
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+          bool ok = key < N;
+          if (MASK == kCausal) ok = ok && key <= qrow;
+          if (MASK == kSliding) ok = ok && key >= qrow - p.wl && key <= qrow + p.wr;
+          if (!ok) s[kb][i] = -INFINITY;
         }
       }
     }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+    mx = halves_max(mx);
+    const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
+    const float mnew = fmaxf(m, mt);
+    const bool resc = mnew > m + kTau;
+    float corr = 1.0f;
+    if (resc) {
+      corr = fast_exp2(m - mnew);
+      m = mnew;
+    }
+    if (__any(resc)) {
+#pragma unroll
+      for (int b = 0; b < DBLK; ++b) scale_in_place(acc[b], corr);
+      l *= corr;
+      lr *= corr;
+    }
+    return (m == -INFINITY) ? 0.0f : m;
+  };
 
-    if (more) swrite(stage ^ 1);
+  // Phase 2: probabilities, rounded to 16 bits in B-operand order, and their
+  // fp32 row sum.
+  auto softmax_exp = [&](f32x16_t s[2], float base, uint32_t pk[2][8]) {
+    float rs[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float e0 = fast_exp2(fmaf(s[kb][2 * j], c, -base));
+        const float e1 = fast_exp2(fmaf(s[kb][2 * j + 1], c, -base));
+        rs[kb] += e0 + e1;
+        pk[kb][j] = Elem<T>::pack2(e0, e1);
+      }
+    l += rs[0] + rs[1];
+  };
+
+  // Phase 3: O^T += V^T P^T over four 16-key steps (DBLK independent chains)
+  // and the row sum of the rounded probabilities.
+  auto pv_sums = [&](int voff, uint32_t pk[2][8]) {
+#pragma unroll
+    for (int ks = 0; ks < BC / 16; ++ks) {
+      const u32x4_t b = {pk[ks >> 1][(ks & 1) * 4 + 0], pk[ks >> 1][(ks & 1) * 4 + 1],
+                         pk[ks >> 1][(ks & 1) * 4 + 2], pk[ks >> 1][(ks & 1) * 4 + 3]};
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db) {
+        const char* va = smem + voff + vr_off[db] + ks * 16 * L::V_PITCH;
+        const u32x2_t lo2 = ld_lds_tr8(va);
+        const u32x2_t hi2 = ld_lds_tr8(va + 8 * L::V_PITCH);
+        const u32x4_t a = {lo2[0], lo2[1], hi2[0], hi2[1]};
+        acc[db] = Elem<T>::mma(a, b, acc[db]);
+      }
+    }
+    float rr[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) rr[kb] = Elem<T>::add_pair(pk[kb][j], rr[kb]);
+    lr += rr[0] + rr[1];
+  };
+
+  // Software pipeline.  Iteration t computes the scores of tile t+1 (K stage
+  // (t+1-lo)%2) while it runs the softmax and the output product of tile t
+  // (V stage (t-lo)%2), so the matrix cores and the vector ALUs have
+  // independent work in the same instruction stream.  Meanwhile K of tile t+2
+  // and V of tile t+1 travel from HBM straight into the LDS stages freed one
+  // iteration ago.  The scores of the (nonexistent) tile after the last are
+  // computed from whatever the stage holds and never used.
+  f32x16_t sA[2], sB[2];
+  gload_k_lds(lo, L::K_STAGE0);
+  gload_v_lds(lo, L::V_STAGE0);
+  if (lo + 1 < hi) gload_k_lds(lo + 1, L::K_STAGE1);
+  wait_vmem();
+  __syncthreads();
+  scores(L::K_STAGE0, sA);
+
+  // One pipeline step; P = (t - lo) % 2 selects the stages at compile time.
+  auto step = [&](auto P_, int t, f32x16_t cur[2], f32x16_t nxt[2]) {
+    constexpr int P = decltype(P_)::value;
+    const bool has1 = t + 1 < hi, has2 = t + 2 < hi;
+    if (has2) gload_k_lds(t + 2, L::kstage(P));
+    if (has1) gload_v_lds(t + 1, L::vstage(1 - P));
+    // A tile with no allowed pair for this wavefront (band edges) is
+    // processed like any other: its probabilities are all zero.
+    const float base = softmax_max(t, cur);
+    uint32_t pk[2][8];
+    scores(L::kstage(1 - P), nxt);
+    softmax_exp(cur, base, pk);
+    interleave_mfma<2 * KSTEPS, 1, 7, 2>();
+    pv_sums(L::vstage(P), pk);
+    interleave_mfma<DBLK * BC / 16, 2, 1, 2>();
+    wait_vmem();
     __syncthreads();
+  };
+  for (int t = lo; t < hi; t += 2) {
+    step(std::integral_constant<int, 0>{}, t, sA, sB);
+    if (t + 1 >= hi) break;
+    step(std::integral_constant<int, 1>{}, t + 1, sB, sA);
   }
 
-  // Epilogue: O = acc / l~ rounded once; lse in natural-log units.
+  // Epilogue: O = acc / l~ rounded once; lse in natural-log units.  Both
+  // halves of the wavefront hold the same l, l~ and m; stores past N drop.
   const float lt = halves_sum(l);
   const float lrt = halves_sum(lr);
-  if (qrow < N) {
-    const float inv = 1.0f / lrt;
-    char* Oh = reinterpret_cast<char*>(p.O) + hoff * 2;
+  const float inv = 1.0f / lrt;
+  const auto rO = make_rsrc(reinterpret_cast<char*>(p.O) + hoff, head_bytes);
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db) {
+  for (int db = 0; db < DBLK; ++db) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x2_t v = {Elem<T>::pack2(acc[db][g * 4 + 0] * inv, acc[db][g * 4 + 1] * inv),
-                           Elem<T>::pack2(acc[db][g * 4 + 2] * inv, acc[db][g * 4 + 3] * inv)};
-        st_global8(Oh + (static_cast<size_t>(qrow) * D + db * 32 + g * 8 + half * 4) * 2, v);
-      }
+    for (int g = 0; g < 4; ++g) {
+      const u32x2_t v = {Elem<T>::pack2(acc[db][g * 4 + 0] * inv, acc[db][g * 4 + 1] * inv),
+                         Elem<T>::pack2(acc[db][g * 4 + 2] * inv, acc[db][g * 4 + 3] * inv)};
+      buf_store8(v, rO, static_cast<uint32_t>(qrow) * ROW_BYTES + (db * 32 + g * 8 + half * 4) * 2);
     }
-    if (half == 0) p.lse[static_cast<size_t>(head) * N + qrow] = (m + log2f(lt)) * kLn2;
   }
+  const auto rL = make_rsrc(p.lse + static_cast<size_t>(head) * N, static_cast<uint32_t>(N) * 4);
+  buf_store4((m + log2f(lt)) * kLn2, rL, static_cast<uint32_t>(qrow) * 4);
 }
 
 template <typename T, int D, int MASK>
 hipError_t launch_one(const FwdParams& p, int64_t n_wg, hipStream_t stream) {
-  constexpr int lds = 2 * 2 * kFwdBlockK * D * 2;
   hipLaunchKernelGGL((fwd_kernel<T, D, MASK>), dim3(static_cast<unsigned>(n_wg)),
-                     dim3(kFwdThreads), lds, stream, p);
+                     dim3(kFwdThreads), FwdLayout<D>::LDS_BYTES, stream, p);
   return hipGetLastError();
 }
 

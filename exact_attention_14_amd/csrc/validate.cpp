@@ -43,6 +43,8 @@ attn_status check_sizes(int dt, int64_t B, int64_t H, int64_t N, int64_t d) {
   // element offsets with 64-bit ones.
   if (B > kMaxI32 || H > kMaxI32 || N > kMaxI32) return ATTN_E_SHAPE;
   if (B * H > kMaxI32) return ATTN_E_SHAPE;
+  // One head's rows are addressed through 32-bit buffer offsets.
+  if (N * d * 2 > kMaxI32) return ATTN_E_SHAPE;
   const int64_t BH = B * H;
   if (BH > (int64_t(1) << 62) / (N * d * 4)) return ATTN_E_SHAPE;
   // Grids: one workgroup per (head, 64-row block) at most.

@@ -147,6 +147,8 @@ int main() {
   CHECK(attn_fwd_check(ATTN_BF16, Q, K, V, O, L, 0, H, N, d, 0.1f, ATTN_MASK_NONE, 0, 0) == ATTN_E_SHAPE, "B");
   CHECK(attn_fwd_check(ATTN_BF16, Q, K, V, O, L, B, H, INT64_MAX, d, 0.1f, ATTN_MASK_NONE, 0, 0) == ATTN_E_SHAPE, "N");
   CHECK(attn_fwd_check(ATTN_BF16, Q, K, V, O, L, INT64_MAX / 2, INT64_MAX / 2, N, d, 0.1f, ATTN_MASK_NONE, 0, 0) == ATTN_E_SHAPE, "BH");
+  CHECK(attn_fwd_check(ATTN_BF16, Q, K, V, O, L, B, H, 8388608, 128, 0.1f, ATTN_MASK_NONE, 0, 0) == ATTN_E_SHAPE, "head bytes");
+  CHECK(attn_fwd_check(ATTN_BF16, Q, K, V, O, L, B, H, 8388607, 128, 0.1f, ATTN_MASK_NONE, 0, 0) == ATTN_E_ALIAS, "head bytes ok (then aliasing of the tiny test buffers)");
   CHECK(attn_fwd_check(ATTN_BF16, Q, K, V, O, L, B, H, N, d, 0.1f, ATTN_MASK_SLIDING, -1, 0) == ATTN_E_MASK, "wl");
   CHECK(attn_fwd_check(ATTN_BF16, Q, K, V, O, L, B, H, N, d, 0.1f, (attn_mask_mode)9, 0, 0) == ATTN_E_MASK, "mode");
   CHECK(attn_fwd_check(ATTN_BF16, Q, K, V, O, L, B, H, N, d, 0.1f, ATTN_MASK_CAUSAL, -5, -5) == ATTN_OK, "windows ignored");
