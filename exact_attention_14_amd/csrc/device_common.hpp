@@ -146,6 +146,16 @@ __device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, char* l
 // direct-to-LDS loads) has completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Waits until at most N of this wavefront's vector-memory operations are
+// still outstanding (they complete in issue order), i.e. everything but the N
+// most recently issued has completed.  s_waitcnt encodes vmcnt in bits 3:0
+// and 15:14; expcnt (bits 6:4) and lgkmcnt (bits 11:8) are left at "any".
+template <int N>
+__device__ __forceinline__ void wait_vmem_but() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
 // Scheduling-group masks for __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedValu = 0x002;
 constexpr int kSchedMfma = 0x008;

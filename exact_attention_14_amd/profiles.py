@@ -1,0 +1,109 @@
+"""Summaries of rocprofv3 output for the committed profiles/ folder.
+
+    python -m exact_attention_14_amd.profiles stats  <kernel_stats.csv> <out.md> <command...>
+    python -m exact_attention_14_amd.profiles traffic <fetch_dir> <write_dir> <workload> <copy_mib> <out.json> <out.md>
+
+``stats`` turns the ``*_kernel_stats.csv`` of ``rocprofv3 --kernel-trace --stats
+--output-format csv`` into a short markdown table.  ``traffic`` reads two
+``rocprofv3 --pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs of ``bench.py
+--copy-calibration-mib M`` and scales the forward kernel's per-dispatch
+counters by what the same counters read for the calibration copy of M MiB
+(a device-to-device copy reads and writes exactly M MiB), giving HBM bytes
+per launch.  The JSON records a hash of the forward kernel's sources so that
+bench.py reports the traffic only while the kernel is unchanged.
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FWD_SOURCES = ("fwd_kernel.hip", "device_common.hpp", "plan.hpp")
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for name in FWD_SOURCES:
+        with open(os.path.join(ROOT, "exact_attention_14_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _demangle_short(name: str) -> str:
+    for key in ("fwd_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "bwd_rowdot_kernel"):
+        if key in name:
+            tail = name.split(key, 1)[1]
+            return key + tail.split("EEvNS")[0].replace("IDF16b", "<bf16,").replace(
+                "IDF16_", "<f16,").replace("Li", "").replace("E", ",") + ">"
+    return name[:60]
+
+
+def stats(csv_path: str, out_md: str, command: str) -> None:
+    rows = list(csv.DictReader(open(csv_path)))
+    lines = ["# rocprofv3 kernel statistics", "", f"Command: `{command}`", "",
+             "| kernel | calls | average (us) | min (us) | max (us) | share |",
+             "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {_demangle_short(r['Name'])} | {r['Calls']} | "
+                     f"{float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+    lines.append("")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines))
+
+
+def _counter(dirname: str, counter: str):
+    """(attn forward values, copy values) per dispatch, in the counter's unit (KiB)."""
+    fwd, copy = [], []
+    for path in glob.glob(os.path.join(dirname, "*counter_collection.csv")):
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"])
+            if "fwd_kernel" in r["Kernel_Name"]:
+                fwd.append(v)
+            elif "copybuffer" in r["Kernel_Name"].lower():
+                copy.append((v, r["Kernel_Name"]))
+    return fwd, copy
+
+
+def traffic(fetch_dir: str, write_dir: str, workload: str, copy_mib: int, out_json: str,
+            out_md: str) -> None:
+    copy_bytes = copy_mib * (1 << 20)
+    out = {"workload": workload, "kernel_source_sha": kernel_source_sha(), "copy_mib": copy_mib}
+    lines = ["# HBM traffic of the forward kernel (rocprofv3 PMC)", "",
+             f"Workload: `{workload}`.  Counters in KiB per dispatch, scaled by the same counter",
+             f"read for a device copy of {copy_mib} MiB (reads and writes exactly that).", ""]
+    total = 0.0
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        fwd, copy = _counter(d, counter)
+        if not fwd or not copy:
+            raise SystemExit(f"missing {counter} values in {d}")
+        copy_val = max(v for v, _ in copy)
+        factor = copy_bytes / (copy_val * 1024.0)
+        per_launch = sum(fwd) / len(fwd) * 1024.0 * factor
+        out[counter] = {"fwd_kib_mean": sum(fwd) / len(fwd), "copy_kib": copy_val,
+                        "scale": factor, "bytes_per_launch": per_launch}
+        total += per_launch
+        lines.append(f"- {counter}: forward {sum(fwd) / len(fwd):.0f} KiB/dispatch (mean of "
+                     f"{len(fwd)}), copy {copy_val:.0f} KiB -> scale {factor:.4f} -> "
+                     f"{per_launch / 1e6:.1f} MB per launch")
+    out["bytes_per_launch"] = total
+    lines += ["", f"Total HBM traffic per launch: {total / 1e6:.1f} MB.", ""]
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=1)
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines))
+
+
+if __name__ == "__main__":
+    if sys.argv[1] == "stats":
+        stats(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
+    elif sys.argv[1] == "traffic":
+        traffic(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5]), sys.argv[6], sys.argv[7])
+    else:
+        raise SystemExit(__doc__)
