@@ -4,12 +4,16 @@
 // §2.2 tiling, §2.3 online softmax, §2.5 teaching kernel; P3 =
 // jsqmd.com/news/1148352 §2 state m, l, O_acc), laid out for CDNA4:
 //
-// * One workgroup = 4 wavefronts = 128 query rows of one head; each wavefront
-//   owns 32 query rows for the whole launch.  K/V are streamed in 64-row
-//   tiles through two-stage LDS rings (P1 §3.2 double-buffered queues),
-//   loaded by direct HBM-to-LDS buffer loads that need no registers.  Loads
-//   and stores go through buffer resources bounded by the head's size, so
-//   rows past N read as zeros and stores past N are dropped without branches.
+// * One workgroup = 8 wavefronts = 256 query rows of one head (two wavefronts
+//   per SIMD); each wavefront owns 32 query rows for the whole launch.  K/V
+//   are streamed in 64-row tiles through two-stage LDS rings (P1 §3.2
+//   double-buffered queues), loaded by direct HBM-to-LDS buffer loads that
+//   need no registers; each tile is fetched once for all 256 rows.  Loads and
+//   stores go through buffer resources bounded by the head's size, so rows
+//   past N read as zeros and stores past N are dropped without branches.
+//   Every LDS stage is an array of its own, so the compiler can tell that
+//   reading one stage does not race the loads in flight into the other and
+//   does not wait for them.
 // * Scores are computed transposed, S^T = K Q^T, on the 32x32x16 matrix
 //   cores: K (A operand) comes from LDS, Q (B operand) stays in registers for
 //   the whole launch.  In the result tile each lane owns one query row and 16
@@ -30,12 +34,16 @@
 // * Scores go straight to the exp2 domain with one FMA, s*c - m, where
 //   c = |scale| * log2(e) (P1 §2.5 and §3.3 (2): exp2 instead of exp).  A
 //   negative scale is folded into Q by flipping its sign bits (exact).
-// * The running max only moves when a tile raises it by more than kTau
-//   (2^kTau in the exp2 domain); otherwise the old max is kept, the
-//   accumulator is not rescaled and probabilities may exceed 1 by at most
-//   2^kTau.  The result is unchanged in exact arithmetic (m cancels between
-//   numerator and l) and nearly all tiles skip the 64 multiplies per lane of
-//   the rescale (P1 §2.3: the rescale corrects history when the max moves).
+// * Optimistic online softmax.  A tile's probabilities are first formed
+//   against the running max m as it stands, without taking the tile's own
+//   row max.  If none of them exceeds 2^kTau (checked through the lane's sum
+//   of them, an upper bound) they are kept: m need not be the exact max, since
+//   it cancels between the numerator and l, and probabilities up to 2^kTau fit
+//   both fp16 and bf16.  Otherwise (and while a row has no m yet) the exact
+//   tile max is taken, m is raised to it, the accumulator, l and l~ are
+//   rescaled (P1 §2.3: the rescale corrects history when the max moves) and
+//   the tile's probabilities are formed again.  Nearly every tile takes the
+//   first path and skips both the row max and the rescale.
 // * Whole key tiles outside the mask's band are never visited (P1 §3.3 (4));
 //   only tiles that straddle the band edge or the ragged end of the sequence
 //   evaluate the mask per element, with -inf (P2 "pitfall 1": ragged lengths;
@@ -58,7 +66,7 @@
 namespace attn {
 namespace {
 
-constexpr float kTau = 8.0f;
+constexpr float kSumBound = 256.0f;  // 2^kTau, kTau = 8
 
 template <int D>
 struct FwdLayout {
@@ -68,21 +76,16 @@ struct FwdLayout {
   static constexpr int V_PITCH = D * 2;
   static constexpr int K_BYTES = BC * K_PITCH;
   static constexpr int V_BYTES = BC * V_PITCH;
-  // Two K stages then two V stages.
-  static constexpr int K_STAGE0 = 0, K_STAGE1 = K_BYTES;
-  static constexpr int V_STAGE0 = 2 * K_BYTES, V_STAGE1 = 2 * K_BYTES + V_BYTES;
-  static constexpr int LDS_BYTES = 2 * K_BYTES + 2 * V_BYTES;
   // K and V go straight to LDS: each wavefront instruction fills 1 KiB.  K
   // rows have NCH + 1 slots of 16 bytes (the last one is padding).
   static constexpr int K_SLOTS = BC * (NCH + 1);
   static constexpr int K_INSTR = K_SLOTS / 64;                 // 17 at d = 128, 9 at d = 64
-  static constexpr int K_INSTR_PER_WAVE = (K_INSTR + 3) / 4;   // waves take j = w, w+4, ...
+  static constexpr int NW = kFwdThreads / 64;
+  static constexpr int K_INSTR_PER_WAVE = (K_INSTR + NW - 1) / NW;
   static constexpr int V_WAVE_LOADS = V_BYTES / (kFwdThreads / 64) / 1024;
   static constexpr int V_ROWS_PER_1K = 1024 / (D * 2);
   static constexpr int VSWZ_MASK = NCH / 4 - 1;             // row bits used by the V swizzle
   static __device__ __forceinline__ int vswz(int row) { return (row & VSWZ_MASK) << 2; }
-  static __host__ __device__ constexpr int kstage(int s) { return s ? K_STAGE1 : K_STAGE0; }
-  static __host__ __device__ constexpr int vstage(int s) { return s ? V_STAGE1 : V_STAGE0; }
 };
 
 template <typename T, int D, int MASK>
@@ -94,7 +97,8 @@ void fwd_kernel(FwdParams p) {
   constexpr int DBLK = D / 32;             // 32-row blocks of O^T
   constexpr uint32_t ROW_BYTES = D * 2;
 
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ __attribute__((aligned(16))) char k_lds0[L::K_BYTES], k_lds1[L::K_BYTES];
+  __shared__ __attribute__((aligned(16))) char v_lds0[L::V_BYTES], v_lds1[L::V_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, half = lane >> 5, r32 = lane & 31;
@@ -130,19 +134,19 @@ void fwd_kernel(FwdParams p) {
   const float c = p.c;
 
   static_assert(L::K_SLOTS % 64 == 0, "K tile must fill whole 1 KiB loads");
-  // K direct loads: instruction j (= wave + 4i) fills 16-byte slots
+  // K direct loads: instruction j (= wave + NW*i, NW wavefronts) fills 16-byte slots
   // s = 64j + lane of the stage; slot s holds row s / (NCH+1), chunk
   // s % (NCH+1).  Padding slots point past the end of the head, so the
   // hardware fills them with zeros without touching memory.
   uint32_t kg_off[L::K_INSTR_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < L::K_INSTR_PER_WAVE; ++i) {
-    const int slot = (wave + 4 * i) * 64 + lane;
+    const int slot = (wave + L::NW * i) * 64 + lane;
     const int row = slot / (L::NCH + 1), ch = slot % (L::NCH + 1);
     kg_off[i] = ch == L::NCH ? head_bytes : static_cast<uint32_t>(row) * ROW_BYTES + ch * 16;
   }
   // V direct loads: instruction j of wavefront w fills LDS bytes
-  // [(4j + w) KiB, +1 KiB) of the stage, i.e. 16-byte slot s = 64*(4j+w) + lane
+  // [(NW*j + w) KiB, +1 KiB) of the stage, i.e. 16-byte slot s = 64*(NW*j+w) + lane
   // = (row, physical chunk); the lane fetches the logical chunk stored there.
   const int vs_slot = wave * 64 + lane;
   const int vs_row = vs_slot / L::NCH, vs_phys = vs_slot % L::NCH;
@@ -163,36 +167,36 @@ void fwd_kernel(FwdParams p) {
     vr_off[db] = row * L::V_PITCH + ((chunk ^ L::vswz(row)) << 4) + (cc & 1) * 8;
   }
 
-  auto gload_k_lds = [&](int t, int off) {
+  auto gload_k_lds = [&](int t, char* dstb) {
     const uint32_t soff = static_cast<uint32_t>(t * BC) * ROW_BYTES;
 #pragma unroll
     for (int i = 0; i < L::K_INSTR_PER_WAVE; ++i) {
-      const int j = wave + 4 * i;
-      if (j < L::K_INSTR) buf_load16_lds(rK, smem + off + j * 1024, kg_off[i], soff);
+      const int j = wave + L::NW * i;
+      if (j < L::K_INSTR) buf_load16_lds(rK, dstb + j * 1024, kg_off[i], soff);
     }
   };
-  auto gload_v_lds = [&](int t, int off) {
+  auto gload_v_lds = [&](int t, char* dstb) {
 #pragma unroll
     for (int j = 0; j < L::V_WAVE_LOADS; ++j)
-      buf_load16_lds(rV, smem + off + (4 * j + wave) * 1024, vg_off,
-                     static_cast<uint32_t>(t * BC + 4 * j * L::V_ROWS_PER_1K) * ROW_BYTES);
+      buf_load16_lds(rV, dstb + (L::NW * j + wave) * 1024, vg_off,
+                     static_cast<uint32_t>(t * BC + L::NW * j * L::V_ROWS_PER_1K) * ROW_BYTES);
   };
 
   // S^T = K Q^T of tile t from a K stage: two independent accumulation chains.
-  auto scores = [&](int koff, f32x16_t s[2]) {
+  auto scores = [&](const char* kb_, f32x16_t s[2]) {
     s[0] = f32x16_t{};
     s[1] = f32x16_t{};
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
-        s[kb] = Elem<T>::mma(ld_lds16(smem + koff + kr_off + kb * 32 * L::K_PITCH + kk * 32),
+        s[kb] = Elem<T>::mma(ld_lds16(kb_ + kr_off + kb * 32 * L::K_PITCH + kk * 32),
                              qf[kk], s[kb]);
   };
 
   // Phase 1 of tile t: mask (boundary tiles only), row max, and the online
   // rescale (rare).  Returns the exponent base.
-  auto softmax_max = [&](int t, f32x16_t s[2]) {
+  auto apply_mask = [&](int t, f32x16_t s[2]) {
     const int k0 = t * BC;
     if (!tile_all_allowed(N, wq0, 32, k0, BC, MASK, p.wl, p.wr)) {
 #pragma unroll
@@ -207,6 +211,10 @@ void fwd_kernel(FwdParams p) {
         }
       }
     }
+  };
+  // Exact row max of the tile (rare path): raises the running max to it and
+  // rescales the accumulator, l and l~.
+  auto raise_max = [&](f32x16_t s[2]) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -215,24 +223,17 @@ void fwd_kernel(FwdParams p) {
     mx = halves_max(mx);
     const float mt = (mx == -INFINITY) ? -INFINITY : mx * c;
     const float mnew = fmaxf(m, mt);
-    const bool resc = mnew > m + kTau;
-    float corr = 1.0f;
-    if (resc) {
-      corr = fast_exp2(m - mnew);
-      m = mnew;
-    }
-    if (__any(resc)) {
+    const float corr = (mnew > m) ? fast_exp2(m - mnew) : 1.0f;
+    m = mnew;
 #pragma unroll
-      for (int b = 0; b < DBLK; ++b) scale_in_place(acc[b], corr);
-      l *= corr;
-      lr *= corr;
-    }
-    return (m == -INFINITY) ? 0.0f : m;
+    for (int b = 0; b < DBLK; ++b) scale_in_place(acc[b], corr);
+    l *= corr;
+    lr *= corr;
   };
 
   // Phase 2: probabilities, rounded to 16 bits in B-operand order, and their
   // fp32 row sum.
-  auto softmax_exp = [&](f32x16_t s[2], float base, uint32_t pk[2][8]) {
+  auto softmax_exp = [&](f32x16_t s[2], float base, uint32_t pk[2][8]) -> float {
     float rs[2] = {0.0f, 0.0f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -243,19 +244,19 @@ void fwd_kernel(FwdParams p) {
         rs[kb] += e0 + e1;
         pk[kb][j] = Elem<T>::pack2(e0, e1);
       }
-    l += rs[0] + rs[1];
+    return rs[0] + rs[1];
   };
 
   // Phase 3: O^T += V^T P^T over four 16-key steps (DBLK independent chains)
   // and the row sum of the rounded probabilities.
-  auto pv_sums = [&](int voff, uint32_t pk[2][8]) {
+  auto pv_sums = [&](const char* vb_, uint32_t pk[2][8]) {
 #pragma unroll
     for (int ks = 0; ks < BC / 16; ++ks) {
       const u32x4_t b = {pk[ks >> 1][(ks & 1) * 4 + 0], pk[ks >> 1][(ks & 1) * 4 + 1],
                          pk[ks >> 1][(ks & 1) * 4 + 2], pk[ks >> 1][(ks & 1) * 4 + 3]};
 #pragma unroll
       for (int db = 0; db < DBLK; ++db) {
-        const char* va = smem + voff + vr_off[db] + ks * 16 * L::V_PITCH;
+        const char* va = vb_ + vr_off[db] + ks * 16 * L::V_PITCH;
         const u32x2_t lo2 = ld_lds_tr8(va);
         const u32x2_t hi2 = ld_lds_tr8(va + 8 * L::V_PITCH);
         const u32x4_t a = {lo2[0], lo2[1], hi2[0], hi2[1]};
@@ -278,27 +279,33 @@ void fwd_kernel(FwdParams p) {
   // iteration ago.  The scores of the (nonexistent) tile after the last are
   // computed from whatever the stage holds and never used.
   f32x16_t sA[2], sB[2];
-  gload_k_lds(lo, L::K_STAGE0);
-  gload_v_lds(lo, L::V_STAGE0);
-  if (lo + 1 < hi) gload_k_lds(lo + 1, L::K_STAGE1);
+  gload_k_lds(lo, k_lds0);
+  gload_v_lds(lo, v_lds0);
+  if (lo + 1 < hi) gload_k_lds(lo + 1, k_lds1);
   wait_vmem();
   __syncthreads();
-  scores(L::K_STAGE0, sA);
+  scores(k_lds0, sA);
 
   // One pipeline step; P = (t - lo) % 2 selects the stages at compile time.
   auto step = [&](auto P_, int t, f32x16_t cur[2], f32x16_t nxt[2]) {
     constexpr int P = decltype(P_)::value;
     const bool has1 = t + 1 < hi, has2 = t + 2 < hi;
-    if (has2) gload_k_lds(t + 2, L::kstage(P));
-    if (has1) gload_v_lds(t + 1, L::vstage(1 - P));
-    // A tile with no allowed pair for this wavefront (band edges) is
-    // processed like any other: its probabilities are all zero.
-    const float base = softmax_max(t, cur);
+    if (has2) gload_k_lds(t + 2, P ? k_lds1 : k_lds0);
+    if (has1) gload_v_lds(t + 1, P ? v_lds0 : v_lds1);
+    apply_mask(t, cur);
     uint32_t pk[2][8];
-    scores(L::kstage(1 - P), nxt);
-    softmax_exp(cur, base, pk);
-    interleave_mfma<2 * KSTEPS, 1, 7, 2>();
-    pv_sums(L::vstage(P), pk);
+    scores(P ? k_lds0 : k_lds1, nxt);
+    float rs = softmax_exp(cur, m == -INFINITY ? 0.0f : m, pk);
+    interleave_mfma<2 * KSTEPS, 1, 6, 2>();
+    // Optimistic softmax: the probabilities used the running max; if one of
+    // them exceeds 2^kTau (their sum does) or the row has no max yet, take
+    // the exact tile max, rescale and recompute (rare).
+    if (__any(!(rs <= kSumBound) || m == -INFINITY)) {
+      raise_max(cur);
+      rs = softmax_exp(cur, m == -INFINITY ? 0.0f : m, pk);
+    }
+    l += rs;
+    pv_sums(P ? v_lds1 : v_lds0, pk);
     interleave_mfma<DBLK * BC / 16, 2, 1, 2>();
     wait_vmem();
     __syncthreads();
@@ -331,7 +338,7 @@ void fwd_kernel(FwdParams p) {
 template <typename T, int D, int MASK>
 hipError_t launch_one(const FwdParams& p, int64_t n_wg, hipStream_t stream) {
   hipLaunchKernelGGL((fwd_kernel<T, D, MASK>), dim3(static_cast<unsigned>(n_wg)),
-                     dim3(kFwdThreads), FwdLayout<D>::LDS_BYTES, stream, p);
+                     dim3(kFwdThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -21,10 +21,10 @@ namespace attn {
 
 enum MaskMode : int { kNone = 0, kCausal = 1, kSliding = 2 };
 
-// Forward tile shape: 4 wavefronts x 32 query rows, 64-row K/V tiles.
-constexpr int kFwdBlockQ = 128;
+// Forward tile shape: 8 wavefronts x 32 query rows, 64-row K/V tiles.
+constexpr int kFwdBlockQ = 256;
 constexpr int kFwdBlockK = 64;
-constexpr int kFwdThreads = 256;
+constexpr int kFwdThreads = 512;
 
 // Backward: the dQ pass mirrors the forward (query-major); the dK/dV pass is
 // key-major with 4 wavefronts x 32 key rows and 64-row query tiles.

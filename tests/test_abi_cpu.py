@@ -62,8 +62,8 @@ def test_launching_entry_points_reject_bad_arguments_before_any_hip_call():
 
 
 def test_fwd_tiles():
-    assert ea.attn_fwd_tiles(128) == (128, 64)
-    assert ea.attn_fwd_tiles(64) == (128, 64)
+    assert ea.attn_fwd_tiles(128) == (256, 64)
+    assert ea.attn_fwd_tiles(64) == (256, 64)
     with pytest.raises(ea.AttnError):
         ea.attn_fwd_tiles(96)
 
