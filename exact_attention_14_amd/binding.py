@@ -59,7 +59,7 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd_workspace_bytes.restype = sz
     L.attn_status_str.argtypes = [i32]
     L.attn_status_str.restype = ctypes.c_char_p
-    L.attn_fwd_tiles.argtypes = [i64, p64, p64]
+    L.attn_fwd_tiles.argtypes = [i64, i32, p64, p64]
     L.attn_fwd_tiles.restype = i32
     L.attn_kv_tile_range.argtypes = [i64, i64, i64, i64, i32, i64, i64, p64, p64]
     L.attn_kv_tile_range.restype = i32
@@ -185,9 +185,9 @@ def attn_kv_tile_range(N, q0, block_q, block_k, mode, wl=0, wr=0):
     return lo.value, hi.value
 
 
-def attn_fwd_tiles(d):
+def attn_fwd_tiles(d, mode=ATTN_MASK_NONE):
     bq, bk = ctypes.c_int64(), ctypes.c_int64()
-    _raise("attn_fwd_tiles", lib().attn_fwd_tiles(d, ctypes.byref(bq), ctypes.byref(bk)))
+    _raise("attn_fwd_tiles", lib().attn_fwd_tiles(d, mode, ctypes.byref(bq), ctypes.byref(bk)))
     return bq.value, bk.value
 
 

@@ -4,11 +4,12 @@
 // §2.2 tiling, §2.3 online softmax, §2.5 teaching kernel; P3 =
 // jsqmd.com/news/1148352 §2 state m, l, O_acc), laid out for CDNA4:
 //
-// * One workgroup = 8 wavefronts = 256 query rows of one head (two wavefronts
-//   per SIMD); each wavefront owns 32 query rows for the whole launch.  K/V
-//   are streamed in 64-row tiles through two-stage LDS rings (P1 §3.2
-//   double-buffered queues), loaded by direct HBM-to-LDS buffer loads that
-//   need no registers; each tile is fetched once for all 256 rows.  Loads and
+// * Each wavefront owns 32 query rows of one head for the whole launch; a
+//   workgroup has 8 of them (256 rows) without a mask and 4 (128 rows) with
+//   a causal or sliding one, at two wavefronts per SIMD.  K/V are streamed
+//   in 64-row tiles through two-stage LDS rings (P1 §3.2 double-buffered
+//   queues), loaded by direct HBM-to-LDS buffer loads that need no
+//   registers; each tile is fetched once for the whole workgroup.  Loads and
 //   stores go through buffer resources bounded by the head's size, so rows
 //   past N read as zeros and stores past N are dropped without branches.
 //   Every LDS stage is an array of its own, so the compiler can tell that
@@ -68,7 +69,7 @@ namespace {
 
 constexpr float kSumBound = 256.0f;  // 2^kTau, kTau = 8
 
-template <int D>
+template <int D, int NWAVES>
 struct FwdLayout {
   static constexpr int BC = kFwdBlockK;
   static constexpr int NCH = D / 8;                  // 16-byte chunks per row
@@ -80,22 +81,23 @@ struct FwdLayout {
   // rows have NCH + 1 slots of 16 bytes (the last one is padding).
   static constexpr int K_SLOTS = BC * (NCH + 1);
   static constexpr int K_INSTR = K_SLOTS / 64;                 // 17 at d = 128, 9 at d = 64
-  static constexpr int NW = kFwdThreads / 64;
+  static constexpr int NW = NWAVES;
   static constexpr int K_INSTR_PER_WAVE = (K_INSTR + NW - 1) / NW;
-  static constexpr int V_WAVE_LOADS = V_BYTES / (kFwdThreads / 64) / 1024;
+  static constexpr int V_WAVE_LOADS = V_BYTES / NW / 1024;
   static constexpr int V_ROWS_PER_1K = 1024 / (D * 2);
   static constexpr int VSWZ_MASK = NCH / 4 - 1;             // row bits used by the V swizzle
   static __device__ __forceinline__ int vswz(int row) { return (row & VSWZ_MASK) << 2; }
 };
 
 template <typename T, int D, int MASK>
-__global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64 * fwd_waves(MASK)) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fwd_kernel(FwdParams p) {
-  using L = FwdLayout<D>;
-  constexpr int BR = kFwdBlockQ, BC = kFwdBlockK;
+  using L = FwdLayout<D, fwd_waves(MASK)>;
+  constexpr int BR = fwd_block_q(MASK), BC = kFwdBlockK;
   constexpr int KSTEPS = D / 16;           // reduction steps over d
   constexpr int DBLK = D / 32;             // 32-row blocks of O^T
   constexpr uint32_t ROW_BYTES = D * 2;
+  constexpr bool kOneSum = std::is_same<T, _Float16>::value;
 
   __shared__ __attribute__((aligned(16))) char k_lds0[L::K_BYTES], k_lds1[L::K_BYTES];
   __shared__ __attribute__((aligned(16))) char v_lds0[L::V_BYTES], v_lds1[L::V_BYTES];
@@ -233,6 +235,11 @@ void fwd_kernel(FwdParams p) {
 
   // Phase 2: probabilities, rounded to 16 bits in B-operand order, and their
   // fp32 row sum.
+  // Probabilities of a tile in the exp2 domain, rounded to 16 bits in
+  // B-operand order, and the lane's sum of them.  For bf16 the sum is over
+  // the fp32 values (bf16 rounding, up to 2^-8 relative, is too coarse for
+  // lse); for fp16 it is over the rounded values (at most 2^-11 relative,
+  // well inside lse's tolerance), so that one sum serves as both l and l~.
   auto softmax_exp = [&](f32x16_t s[2], float base, uint32_t pk[2][8]) -> float {
     float rs[2] = {0.0f, 0.0f};
 #pragma unroll
@@ -241,8 +248,11 @@ void fwd_kernel(FwdParams p) {
       for (int j = 0; j < 8; ++j) {
         const float e0 = fast_exp2(fmaf(s[kb][2 * j], c, -base));
         const float e1 = fast_exp2(fmaf(s[kb][2 * j + 1], c, -base));
-        rs[kb] += e0 + e1;
         pk[kb][j] = Elem<T>::pack2(e0, e1);
+        if (kOneSum)
+          rs[kb] = Elem<T>::add_pair(pk[kb][j], rs[kb]);
+        else
+          rs[kb] += e0 + e1;
       }
     return rs[0] + rs[1];
   };
@@ -263,12 +273,14 @@ void fwd_kernel(FwdParams p) {
         acc[db] = Elem<T>::mma(a, b, acc[db]);
       }
     }
-    float rr[2] = {0.0f, 0.0f};
+    if (!kOneSum) {
+      float rr[2] = {0.0f, 0.0f};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) rr[kb] = Elem<T>::add_pair(pk[kb][j], rr[kb]);
-    lr += rr[0] + rr[1];
+        for (int j = 0; j < 8; ++j) rr[kb] = Elem<T>::add_pair(pk[kb][j], rr[kb]);
+      lr += rr[0] + rr[1];
+    }
   };
 
   // Software pipeline.  Iteration t computes the scores of tile t+1 (K stage
@@ -319,7 +331,7 @@ void fwd_kernel(FwdParams p) {
   // Epilogue: O = acc / l~ rounded once; lse in natural-log units.  Both
   // halves of the wavefront hold the same l, l~ and m; stores past N drop.
   const float lt = halves_sum(l);
-  const float lrt = halves_sum(lr);
+  const float lrt = kOneSum ? lt : halves_sum(lr);
   const float inv = 1.0f / lrt;
   const auto rO = make_rsrc(reinterpret_cast<char*>(p.O) + hoff, head_bytes);
 #pragma unroll
@@ -338,7 +350,7 @@ void fwd_kernel(FwdParams p) {
 template <typename T, int D, int MASK>
 hipError_t launch_one(const FwdParams& p, int64_t n_wg, hipStream_t stream) {
   hipLaunchKernelGGL((fwd_kernel<T, D, MASK>), dim3(static_cast<unsigned>(n_wg)),
-                     dim3(kFwdThreads), 0, stream, p);
+                     dim3(64 * fwd_waves(MASK)), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -14,7 +14,7 @@ struct FwdParams {
   float* lse;
   int N;          // rows per head
   int n_heads;    // B * H
-  int n_qblk;     // ceil(N / kFwdBlockQ)
+  int n_qblk;     // ceil(N / fwd_block_q(mode))
   int wl, wr;     // windows clipped to [0, N] (sliding only)
   float c;        // |scale| * log2(e), at least 1e-30 (see launch code)
   uint32_t qsign; // 0x80008000 flips the sign of both 16-bit halves of a word

@@ -40,7 +40,7 @@ attn_status attn_fwd(attn_dtype dt, const void* Q, const void* K, const void* V,
   p.Q = Q; p.K = K; p.V = V; p.O = O; p.lse = lse;
   p.N = static_cast<int>(N);
   p.n_heads = static_cast<int>(B * H);
-  p.n_qblk = static_cast<int>(attn::ceil_div(N, attn::kFwdBlockQ));
+  p.n_qblk = static_cast<int>(attn::ceil_div(N, attn::fwd_block_q(mode)));
   p.wl = mode == ATTN_MASK_SLIDING ? attn::clip_window(window_left, N) : 0;
   p.wr = mode == ATTN_MASK_SLIDING ? attn::clip_window(window_right, N) : 0;
   p.c = attn::exp2_coeff(scale);

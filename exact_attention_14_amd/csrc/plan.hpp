@@ -21,10 +21,14 @@ namespace attn {
 
 enum MaskMode : int { kNone = 0, kCausal = 1, kSliding = 2 };
 
-// Forward tile shape: 8 wavefronts x 32 query rows, 64-row K/V tiles.
-constexpr int kFwdBlockQ = 256;
+// Forward tile shape: 64-row K/V tiles; workgroups of 32-row wavefronts.
+// Without a mask a workgroup has 8 wavefronts (256 query rows) so that each
+// K/V tile is fetched once for more rows; with a causal or sliding mask it
+// has 4 (128 rows), whose finer work items balance the unequal row lengths
+// and waste fewer products on tiles past a wavefront's band.
 constexpr int kFwdBlockK = 64;
-constexpr int kFwdThreads = 512;
+ATTN_HD constexpr int fwd_waves(int mode) { return mode == 0 ? 8 : 4; }
+ATTN_HD constexpr int fwd_block_q(int mode) { return 32 * fwd_waves(mode); }
 
 // Backward: the dQ pass mirrors the forward (query-major); the dK/dV pass is
 // key-major with 4 wavefronts x 32 key rows and 64-row query tiles.

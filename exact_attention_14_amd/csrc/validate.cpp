@@ -177,10 +177,11 @@ attn_status attn_bwd_check(attn_dtype dt, const void* Q, const void* K, const vo
                          d, scale, mode, window_left, window_right);
 }
 
-attn_status attn_fwd_tiles(int64_t d, int64_t* block_q, int64_t* block_k) {
+attn_status attn_fwd_tiles(int64_t d, attn_mask_mode mode, int64_t* block_q, int64_t* block_k) {
   if (block_q == nullptr || block_k == nullptr) return ATTN_E_NULLPTR;
   if (d != 64 && d != 128) return ATTN_E_UNSUPPORTED;
-  *block_q = attn::kFwdBlockQ;
+  if (attn::check_mask(mode, 0, 0) != ATTN_OK) return ATTN_E_MASK;
+  *block_q = attn::fwd_block_q(mode);
   *block_k = attn::kFwdBlockK;
   return ATTN_OK;
 }

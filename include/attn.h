@@ -155,9 +155,11 @@ attn_status attn_bwd_check(attn_dtype dt, const void* Q, const void* K, const vo
 /*
  * attn_fwd_tiles -- the forward's tile shape: *block_q query rows per
  * workgroup (Br) and *block_k key rows per streamed K/V tile (Bc) for head
- * size d (P1 §2.2).  Returns ATTN_E_UNSUPPORTED for other d.
+ * size d and mask mode (P1 §2.2).  Br is 256 without a mask and 128 with a
+ * causal or sliding mask; Bc is 64.  Returns ATTN_E_UNSUPPORTED for other d,
+ * ATTN_E_MASK for an unknown mode.
  */
-attn_status attn_fwd_tiles(int64_t d, int64_t* block_q, int64_t* block_k);
+attn_status attn_fwd_tiles(int64_t d, attn_mask_mode mode, int64_t* block_q, int64_t* block_k);
 
 /*
  * attn_kv_tile_range -- the half-open range [*lo, *hi) of key tiles (of

@@ -62,10 +62,14 @@ def test_launching_entry_points_reject_bad_arguments_before_any_hip_call():
 
 
 def test_fwd_tiles():
-    assert ea.attn_fwd_tiles(128) == (256, 64)
-    assert ea.attn_fwd_tiles(64) == (256, 64)
+    for d in (64, 128):
+        assert ea.attn_fwd_tiles(d, 0) == (256, 64)
+        assert ea.attn_fwd_tiles(d, 1) == (128, 64)
+        assert ea.attn_fwd_tiles(d, 2) == (128, 64)
     with pytest.raises(ea.AttnError):
         ea.attn_fwd_tiles(96)
+    with pytest.raises(ea.AttnError):
+        ea.attn_fwd_tiles(128, 3)
 
 
 @pytest.mark.parametrize("N", [1, 17, 128, 333, 1000])
@@ -74,7 +78,7 @@ def test_kv_tile_range_matches_the_oracle_mask(N, mask):
     """Every visited tile holds an allowed pair and every allowed pair is in a visited tile."""
     mode, wl, wr = ea.mask_args(mask)
     name = ["none", "causal", "sliding"][mode]
-    bq, bk = ea.attn_fwd_tiles(128)
+    bq, bk = ea.attn_fwd_tiles(128, mode)
     keys = np.arange(N)
     for q0 in range(0, N, bq):
         lo, hi = ea.attn_kv_tile_range(N, q0, bq, bk, mode, wl, wr)
