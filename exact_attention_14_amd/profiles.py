@@ -2,6 +2,7 @@
 
     python -m exact_attention_14_amd.profiles stats  <kernel_stats.csv> <out.md> <command...>
     python -m exact_attention_14_amd.profiles traffic <fetch_dir> <write_dir> <workload> <copy_mib> <out.json> <out.md>
+    python -m exact_attention_14_amd.profiles counters <counter_dir> <kernel_stats.csv> <out.md> <command...>
 
 ``stats`` turns the ``*_kernel_stats.csv`` of ``rocprofv3 --kernel-trace --stats
 --output-format csv`` into a short markdown table.  ``traffic`` reads two
@@ -10,7 +11,10 @@
 counters by what the same counters read for the calibration copy of M MiB
 (a device-to-device copy reads and writes exactly M MiB), giving HBM bytes
 per launch.  The JSON records a hash of the forward kernel's sources so that
-bench.py reports the traffic only while the kernel is unchanged.
+bench.py reports the traffic only while the kernel is unchanged.  ``counters``
+summarises one ``--pmc`` pass over the forward (per-dispatch means) and
+derives its clock and matrix-core busy fraction: GRBM_GUI_ACTIVE is summed
+over the 8 dies and SQ_VALU_MFMA_BUSY_CYCLES over the 1024 SIMDs.
 """
 from __future__ import annotations
 
@@ -100,9 +104,38 @@ def traffic(fetch_dir: str, write_dir: str, workload: str, copy_mib: int, out_js
         f.write("\n".join(lines))
 
 
+def counters(counter_dir: str, kernel_stats: str, out_md: str, command: str) -> None:
+    per = {}
+    for path in glob.glob(os.path.join(counter_dir, "*counter_collection.csv")):
+        for r in csv.DictReader(open(path)):
+            if "fwd_kernel" not in r["Kernel_Name"]:
+                continue
+            per.setdefault(r["Counter_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
+            per[r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    mean = {k: sum(v.values()) / len(v) for k, v in per.items()}
+    avg_ns = [float(r["AverageNs"]) for r in csv.DictReader(open(kernel_stats))
+              if "fwd_kernel" in r["Name"]][0]
+    lines = ["# Forward kernel counters (rocprofv3 PMC)", "", f"Command: `{command}`", "",
+             f"Kernel duration (average from the kernel trace of the same workload): "
+             f"{avg_ns / 1e3:.1f} us", "", "| counter | mean per dispatch |", "|---|---|"]
+    lines += [f"| {k} | {v:.4g} |" for k, v in sorted(mean.items())]
+    if "GRBM_GUI_ACTIVE" in mean:
+        cycles = mean["GRBM_GUI_ACTIVE"] / 8
+        lines += ["", f"- cycles per die: {cycles:.4g}; clock = cycles / duration = "
+                      f"{cycles / avg_ns:.2f} GHz"]
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+            lines.append(f"- matrix cores busy: {mean['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024 / cycles:.1%}"
+                         " of cycles (per SIMD)")
+    lines.append("")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines))
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         stats(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
+    elif sys.argv[1] == "counters":
+        counters(sys.argv[2], sys.argv[3], sys.argv[4], " ".join(sys.argv[5:]))
     elif sys.argv[1] == "traffic":
         traffic(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5]), sys.argv[6], sys.argv[7])
     else:
