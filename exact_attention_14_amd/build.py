@@ -22,6 +22,11 @@ LIB = os.path.join(PKG, "libattn.so")
 
 ARCH = "gfx950"
 HIP_SOURCES = ["fwd_kernel.hip", "bwd_kernels.hip", "launch.hip"]
+# The backward's key-major kernel keeps its dV/dK accumulators in AGPRs
+# (inline-asm matrix instructions) and its score tiles in VGPRs; the
+# compiler's own matrix instructions must then use the VGPR form, or it would
+# place the score tiles in AGPRs and copy them out for the vector code.
+EXTRA_FLAGS = {"bwd_kernels.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 CXX_SOURCES = ["validate.cpp"]
 
 # Packed fp32 arithmetic is disabled for every device compile.
@@ -53,7 +58,8 @@ def build(verbose: bool = False) -> str:
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
         objs.append(obj)
-        jobs.append([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([hipcc, *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
+                     "-o", obj])
     for src in CXX_SOURCES:
         obj = os.path.join(BUILD, src + ".o")
         objs.append(obj)

@@ -8,17 +8,24 @@
 //
 // Three launches, no atomics, so the result is deterministic:
 //   1. bwd_rowdot:  D_i = dO_i . O_i from the forward's stored O (fp32).
-//   2. bwd_dq:      query-major like the forward.  Per 64-key tile:
-//                   S^T = K Q^T, P^T, dP^T = V dO^T, dS^T = P^T (dP^T - D),
-//                   dQ^T += K^T dS^T.  Q and dO stay in registers.
-//   3. bwd_dkdv:    key-major.  Per 64-query tile: S = Q K^T, P,
-//                   dP = dO V^T, dS = P (dP - D), dV^T += dO^T P,
-//                   dK^T += Q^T dS.  K and V stay in registers.
-// The matrix-core layouts are those of device_common.hpp: a 32x32 result
-// tile feeds the next product as its B operand when its rows are the next
-// reduction index, and operands read along that index are stored transposed
-// in LDS in the matching perm16 order.  All products accumulate in fp32; P
-// and dS are rounded to the storage type before they enter a product.
+//   2. bwd_dq:      query-major like the forward.  Per 64-key tile, 32 keys
+//                   at a time: S^T = K Q^T, P^T, dP^T = V dO^T,
+//                   dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.  Q and dO stay
+//                   in registers; two wavefronts per SIMD.
+//   3. bwd_dkdv:    key-major.  Per 64-query tile, 32 queries at a time:
+//                   S = Q K^T, P, dP = dO V^T, dS = P (dP - D),
+//                   dV^T += dO^T P, dK^T += Q^T dS.  K and V stay in
+//                   registers; one wavefront per SIMD (the four accumulator
+//                   sets do not fit two).
+// Tiles stream through double-buffered LDS stages filled by direct
+// HBM-to-LDS loads (one array per stage, so reading one stage never waits
+// for the loads into the other).  Each 64-row tile is stored once, row-major
+// with its 16-byte chunks permuted per row, and read both ways: as rows with
+// 16-byte reads (operands whose reduction index is d) and transposed with
+// ds_read_b64_tr_b16 (operands whose reduction index is the tile's rows).
+// The permutation is chosen so that both read patterns are free of LDS bank
+// conflicts.  All products accumulate in fp32; P and dS are rounded to the
+// storage type before they enter a product.
 #include <hip/hip_runtime.h>
 
 #include "device_common.hpp"
@@ -50,82 +57,126 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(BwdParams p, int64_t ro
   if (row < rows && ch == 0) p.Dsum[row] = acc;
 }
 
-// Shared loaders --------------------------------------------------------
-// A 64-row tile of [rows][D] elements is loaded by threads tid < 16 * NCH,
-// each owning 4 consecutive rows of one 16-byte chunk, and written to LDS
-// either as rows (XOR-swizzled chunks) or transposed (one LDS row per d
-// index, the 64 rows at perm16 positions, chunks swizzled by the d index).
+// A 64-row tile of a [rows][D] 16-bit matrix in LDS: row-major, 16-byte
+// chunk c of row r stored at chunk position c ^ swz(r).
+//  * Row reads (lane r of a 16-lane group reads one chunk of row r0 + r):
+//    swz takes 16 distinct values over any 16 consecutive rows (d = 128) or
+//    8 over the rows of one parity (d = 64, two rows per 256-byte bank line),
+//    so the 16 lanes cover all 64 banks.
+//  * Transposing reads (32 lanes read four consecutive rows x four aligned
+//    chunks): the four rows' swz values differ in the bits that select the
+//    aligned group of four chunks, so the rows land in disjoint banks.
 template <int D>
-struct Tile64 {
-  static constexpr int NCH = D / 8;
-  static constexpr int KSWZ = NCH < 16 ? NCH : 16;
-  static constexpr int BYTES = 64 * D * 2;
-  static constexpr int T_PITCH = 64 * 2;
-  static constexpr int LOADERS = 16 * NCH;
+struct BwdTile {
+  static constexpr int NCH = D / 8;         // 16-byte chunks per row
+  static constexpr int ROWB = D * 2;        // bytes per row
+  static constexpr int BYTES = 64 * ROWB;
+  static constexpr int INSTR = BYTES / 1024;  // 1 KiB direct loads per tile
+  static constexpr int R1K = 1024 / ROWB;     // rows per direct load
+  static __device__ __forceinline__ int swz(int r) {
+    return NCH == 16 ? (((r & 3) << 2) | ((r >> 2) & 3))
+                     : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+  }
+  static __device__ __forceinline__ int off(int row, int chunk) {
+    return row * ROWB + ((chunk ^ swz(row)) << 4);
+  }
+};
 
-  static __device__ __forceinline__ int row_off(int row, int ch) {
-    return (row * NCH + (ch ^ (row & (KSWZ - 1)))) * 16;
+// Direct loads of one tile by NW wavefronts: instruction j = w + NW*i fills
+// LDS bytes [j KiB, +1 KiB), i.e. rows j*R1K + lane/NCH at chunk position
+// lane % NCH, fetching the logical chunk stored there.  swz depends on the
+// row's low four bits only, which the NW*R1K-row stride between a
+// wavefront's instructions leaves unchanged, so one per-lane offset serves.
+template <int D, int NW>
+struct TileLoader {
+  using L = BwdTile<D>;
+  static constexpr int PER_WAVE = L::INSTR / NW;
+  static_assert(L::INSTR % NW == 0 && (NW * L::R1K) % 16 == 0, "loader geometry");
+  uint32_t voff;
+  int wave;
+  __device__ TileLoader(int wave_, int lane) : wave(wave_) {
+    const int row = wave_ * L::R1K + lane / L::NCH;
+    voff = static_cast<uint32_t>(row) * L::ROWB +
+           static_cast<uint32_t>(((lane % L::NCH) ^ L::swz(row)) << 4);
   }
-  static __device__ __forceinline__ int tr_off(int drow, int chunk) {
-    return drow * T_PITCH + ((chunk ^ (drow & 7)) << 4);
-  }
-  // Loads rows r0 + 4*rg .. +3, chunk ch of a [N][D] matrix (zeros past N).
-  static __device__ __forceinline__ void load(u32x4_t v[4], const char* base, int r0, int N,
-                                              int rg, int ch, uint32_t sign = 0) {
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, char* dst, int row0) const {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int row = r0 + rg * 4 + r;
-      v[r] = row < N ? (ld_global16(base + (static_cast<size_t>(row) * D + ch * 8) * 2) ^ sign)
-                     : u32x4_t{0, 0, 0, 0};
-    }
+    for (int i = 0; i < PER_WAVE; ++i)
+      buf_load16_lds(r, dst + (wave + NW * i) * 1024, voff,
+                     static_cast<uint32_t>(row0 + NW * i * L::R1K) * L::ROWB);
   }
-  static __device__ __forceinline__ void store_rows(char* lds, const u32x4_t v[4], int rg, int ch) {
+};
+
+// Per-lane offsets of the two read patterns (relative to a tile and to the
+// 32-row block / 16-row step selected by an immediate added by the caller).
+template <int D>
+struct TileReaders {
+  using L = BwdTile<D>;
+  static constexpr int KSTEPS = D / 16, DBLK = D / 32;
+  // Row reads, A operand of a product reducing over d: lane (r, half) reads
+  // row r, chunk 2kk + half.
+  int row[KSTEPS];
+  // Transposing reads, A operand of a product reducing over the tile's rows:
+  // lane (group G, t, cc) reads rows 4*half + t and 4*half + t + 8 of a 16-row
+  // step, columns 32db + 16(G%2) + 4cc .. +3.
+  int tr[DBLK][2];
+  __device__ TileReaders(int lane) {
+    const int half = lane >> 5, r32 = lane & 31;
+    const int G = lane >> 4, tt = (lane >> 2) & 3, cc = lane & 3;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) st_lds16(lds + row_off(rg * 4 + r, ch), v[r]);
+    for (int kk = 0; kk < KSTEPS; ++kk) row[kk] = L::off(r32, 2 * kk + half);
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        tr[db][h] = L::off(4 * half + tt + 8 * h, 4 * db + 2 * (G & 1) + (cc >> 1)) + (cc & 1) * 8;
   }
-  static __device__ __forceinline__ void store_transposed(char* lds, const u32x4_t v[4], int rg,
-                                                          int ch) {
-    const int pos = perm16(rg * 4);
-    const int chunk = pos >> 3, sub = (pos & 7) * 2;
-    write_transposed_4x8(lds, v, ch * 8, [&](int drow) {
-      return drow * T_PITCH + ((chunk ^ (drow & 7)) << 4) + sub;
-    });
+  // 32 x 16 A operand, rows blk*32 .., chunk pair kk.
+  __device__ __forceinline__ u32x4_t rows(const char* tile, int blk, int kk) const {
+    return ld_lds16(tile + row[kk] + blk * 32 * L::ROWB);
+  }
+  // 32 x 16 A operand of the transpose: d block db, tile rows 16*st .. +15.
+  __device__ __forceinline__ u32x4_t trans(const char* tile, int db, int st) const {
+    const u32x2_t lo2 = ld_lds_tr8(tile + tr[db][0] + st * 16 * L::ROWB);
+    const u32x2_t hi2 = ld_lds_tr8(tile + tr[db][1] + st * 16 * L::ROWB);
+    return u32x4_t{lo2[0], lo2[1], hi2[0], hi2[1]};
   }
 };
 
 // ------------------------------------------------------------------ dQ
 template <typename T, int D, int MASK>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdParams p, int n_qblk) {
-  using L = Tile64<D>;
-  constexpr int BQ = kBwdDqBlockQ, BK = kBwdDqBlockK;
-  static_assert(BK == 64, "tile loader assumes 64-row tiles");
-  constexpr int KSTEPS = D / 16, DBLK = D / 32, NCH = D / 8;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  char* k_rows = smem;
-  char* k_tr = smem + L::BYTES;
-  char* v_rows = smem + 2 * L::BYTES;
+  using L = BwdTile<D>;
+  constexpr int BQ = kBwdDqBlockQ, BK = kBwdDqBlockK, NW = kBwdThreads / 64;
+  static_assert(BK == 64 && BQ == 32 * NW, "dQ tile geometry");
+  constexpr int KSTEPS = D / 16, DBLK = D / 32;
+  constexpr uint32_t ROWB = L::ROWB;
+  __shared__ __attribute__((aligned(16))) char k_lds0[L::BYTES], k_lds1[L::BYTES];
+  __shared__ __attribute__((aligned(16))) char v_lds0[L::BYTES], v_lds1[L::BYTES];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, r32 = lane & 31;
+  const int lane = tid & 63, half = lane >> 5, r32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int N = p.N;
   int64_t head, qblk;
   fwd_work_item(blockIdx.x, p.n_heads, n_qblk, MASK, &head, &qblk);
   const int q0 = static_cast<int>(qblk) * BQ;
-  const size_t hoff = static_cast<size_t>(head) * N * D;
-  const char* Qh = reinterpret_cast<const char*>(p.Q) + hoff * 2;
-  const char* Kh = reinterpret_cast<const char*>(p.K) + hoff * 2;
-  const char* Vh = reinterpret_cast<const char*>(p.V) + hoff * 2;
-  const char* dOh = reinterpret_cast<const char*>(p.dO) + hoff * 2;
+  const size_t hoff = static_cast<size_t>(head) * N * D * 2;
+  const uint32_t head_bytes = static_cast<uint32_t>(N) * ROWB;
+  const auto rQ = make_rsrc(reinterpret_cast<const char*>(p.Q) + hoff, head_bytes);
+  const auto rK = make_rsrc(reinterpret_cast<const char*>(p.K) + hoff, head_bytes);
+  const auto rV = make_rsrc(reinterpret_cast<const char*>(p.V) + hoff, head_bytes);
+  const auto rG = make_rsrc(reinterpret_cast<const char*>(p.dO) + hoff, head_bytes);
 
   const int wq0 = q0 + wave * 32;
   const int qrow = wq0 + r32;
   u32x4_t qf[KSTEPS], gf[KSTEPS];
 #pragma unroll
   for (int kk = 0; kk < KSTEPS; ++kk) {
-    const size_t off = (static_cast<size_t>(qrow) * D + kk * 16 + half * 8) * 2;
-    qf[kk] = qrow < N ? (ld_global16(Qh + off) ^ p.qsign) : u32x4_t{0, 0, 0, 0};
-    gf[kk] = qrow < N ? ld_global16(dOh + off) : u32x4_t{0, 0, 0, 0};
+    const uint32_t off = static_cast<uint32_t>(qrow) * ROWB + kk * 32 + half * 16;
+    qf[kk] = buf_load16(rQ, off, 0) ^ p.qsign;
+    gf[kk] = buf_load16(rG, off, 0);
   }
   const float lse2 = qrow < N ? p.lse[static_cast<size_t>(head) * N + qrow] * kLog2e : INFINITY;
   const float Dq = qrow < N ? p.Dsum[static_cast<size_t>(head) * N + qrow] : 0.0f;
@@ -135,38 +186,27 @@ void bwd_dq_kernel(BwdParams p, int n_qblk) {
 #pragma unroll
   for (int b = 0; b < DBLK; ++b) acc[b] = f32x16_t{};
 
-  int64_t lo, hi;
-  kv_tile_range(N, q0, BQ, BK, MASK, p.wl, p.wr, &lo, &hi);
-  const bool loader = tid < L::LOADERS;
-  const int rg = tid / NCH, ch = tid % NCH;
+  int64_t lo64, hi64;
+  kv_tile_range(N, q0, BQ, BK, MASK, p.wl, p.wr, &lo64, &hi64);
+  const int lo = static_cast<int>(lo64), hi = static_cast<int>(hi64);
+  const TileLoader<D, NW> ld(wave, lane);
+  const TileReaders<D> rd(lane);
 
-  for (int t = static_cast<int>(lo); t < static_cast<int>(hi); ++t) {
+  // One key tile from a pair of stages: 32 keys at a time, S^T and dP^T,
+  // then dS^T, then dQ^T += K^T dS^T over the block's two 16-key steps.
+  auto tile = [&](int t, const char* kt, const char* vt) {
     const int k0 = t * BK;
-    u32x4_t kv[4], vv[4];
-    if (loader) {
-      L::load(kv, Kh, k0, N, rg, ch);
-      L::load(vv, Vh, k0, N, rg, ch);
-    }
-    __syncthreads();
-    if (loader) {
-      L::store_rows(k_rows, kv, rg, ch);
-      L::store_transposed(k_tr, kv, rg, ch);
-      L::store_rows(v_rows, vv, rg, ch);
-    }
-    __syncthreads();
-    if (tile_none_allowed(N, wq0, 32, k0, BK, MASK, p.wl, p.wr)) continue;
+    if (MASK != kNone && tile_none_allowed(N, wq0, 32, k0, BK, MASK, p.wl, p.wr)) return;
     const bool full = tile_all_allowed(N, wq0, 32, k0, BK, MASK, p.wl, p.wr);
-
-    uint32_t ds[2][8];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       f32x16_t s = f32x16_t{}, dp = f32x16_t{};
-      const int row = kb * 32 + r32;
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
-        s = Elem<T>::mma(ld_lds16(k_rows + L::row_off(row, kk * 2 + half)), qf[kk], s);
-        dp = Elem<T>::mma(ld_lds16(v_rows + L::row_off(row, kk * 2 + half)), gf[kk], dp);
+        s = Elem<T>::mma(rd.rows(kt, kb, kk), qf[kk], s);
+        dp = Elem<T>::mma(rd.rows(vt, kb, kk), gf[kk], dp);
       }
+      uint32_t ds[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         float e[2];
@@ -180,183 +220,235 @@ void bwd_dq_kernel(BwdParams p, int n_qblk) {
             if (MASK == kCausal) ok = ok && key <= qrow;
             if (MASK == kSliding) ok = ok && key >= qrow - p.wl && key <= qrow + p.wr;
           }
-          const float pr = ok ? fast_exp2(fmaf(s[i], c, -lse2)) : 0.0f;
+          float pr = fast_exp2(fmaf(s[i], c, -lse2));
+          if (!ok) pr = 0.0f;  // a select, not a branch
           e[u] = pr * (dp[i] - Dq);
         }
-        ds[kb][j] = Elem<T>::pack2(e[0], e[1]);
+        ds[j] = Elem<T>::pack2(e[0], e[1]);
       }
-    }
-    // dQ^T += K^T dS^T
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const u32x4_t b = {ds[kk >> 1][(kk & 1) * 4 + 0], ds[kk >> 1][(kk & 1) * 4 + 1],
-                         ds[kk >> 1][(kk & 1) * 4 + 2], ds[kk >> 1][(kk & 1) * 4 + 3]};
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const u32x4_t b = {ds[h2 * 4 + 0], ds[h2 * 4 + 1], ds[h2 * 4 + 2], ds[h2 * 4 + 3]};
 #pragma unroll
-      for (int db = 0; db < DBLK; ++db)
-        acc[db] = Elem<T>::mma(ld_lds16(k_tr + L::tr_off(db * 32 + r32, kk * 2 + half)), b, acc[db]);
+        for (int db = 0; db < DBLK; ++db)
+          acc[db] = Elem<T>::mma(rd.trans(kt, db, kb * 2 + h2), b, acc[db]);
+      }
+      // Keeps the two 32-key blocks from being interleaved (register
+      // pressure: each block holds its own S^T, dP^T and operand reads).
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  ld.load(rK, k_lds0, lo * BK);
+  ld.load(rV, v_lds0, lo * BK);
+  wait_vmem();
+  __syncthreads();
+  for (int t = lo; t < hi; t += 2) {
+    if (t + 1 < hi) {
+      ld.load(rK, k_lds1, (t + 1) * BK);
+      ld.load(rV, v_lds1, (t + 1) * BK);
+    }
+    tile(t, k_lds0, v_lds0);
+    wait_vmem();
+    __syncthreads();
+    if (t + 1 >= hi) break;
+    if (t + 2 < hi) {
+      ld.load(rK, k_lds0, (t + 2) * BK);
+      ld.load(rV, v_lds0, (t + 2) * BK);
+    }
+    tile(t + 1, k_lds1, v_lds1);
+    wait_vmem();
+    __syncthreads();
   }
 
-  if (qrow < N) {
-    char* dQh = reinterpret_cast<char*>(p.dQ) + hoff * 2;
-    const float sc = p.scale;
+  // dQ = scale * dS K; stores past N are dropped by the buffer bound.
+  const auto rdQ = make_rsrc(reinterpret_cast<char*>(p.dQ) + hoff, head_bytes);
+  const float sc = p.scale;
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db)
+  for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x2_t v = {Elem<T>::pack2(acc[db][g * 4 + 0] * sc, acc[db][g * 4 + 1] * sc),
-                           Elem<T>::pack2(acc[db][g * 4 + 2] * sc, acc[db][g * 4 + 3] * sc)};
-        st_global8(dQh + (static_cast<size_t>(qrow) * D + db * 32 + g * 8 + half * 4) * 2, v);
-      }
-  }
+    for (int g = 0; g < 4; ++g) {
+      const u32x2_t v = {Elem<T>::pack2(acc[db][g * 4 + 0] * sc, acc[db][g * 4 + 1] * sc),
+                         Elem<T>::pack2(acc[db][g * 4 + 2] * sc, acc[db][g * 4 + 3] * sc)};
+      buf_store8(v, rdQ, static_cast<uint32_t>(qrow) * ROWB + (db * 32 + g * 8 + half * 4) * 2);
+    }
 }
 
 // ---------------------------------------------------------------- dK, dV
 template <typename T, int D, int MASK>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
-  using L = Tile64<D>;
-  constexpr int BK = kBwdKvBlockK, BQ = kBwdKvBlockQ;
-  static_assert(BQ == 64, "tile loader assumes 64-row tiles");
-  constexpr int KSTEPS = D / 16, DBLK = D / 32, NCH = D / 8;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  char* q_rows = smem;
-  char* q_tr = smem + L::BYTES;
-  char* g_rows = smem + 2 * L::BYTES;
-  char* g_tr = smem + 3 * L::BYTES;
-  float* lse_t = reinterpret_cast<float*>(smem + 4 * L::BYTES);
-  float* D_t = lse_t + 64;
+  using L = BwdTile<D>;
+  constexpr int BK = kBwdKvBlockK, BQ = kBwdKvBlockQ, NW = kBwdThreads / 64;
+  static_assert(BQ == 64 && BK == 32 * NW, "dK/dV tile geometry");
+  constexpr int KSTEPS = D / 16, DBLK = D / 32;
+  constexpr uint32_t ROWB = L::ROWB;
+  __shared__ __attribute__((aligned(16))) char q_lds0[L::BYTES], q_lds1[L::BYTES];
+  __shared__ __attribute__((aligned(16))) char g_lds0[L::BYTES], g_lds1[L::BYTES];
+  __shared__ __attribute__((aligned(16))) float s_lse0[BQ], s_lse1[BQ], s_d0[BQ], s_d1[BQ];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, half = lane >> 5, r32 = lane & 31;
+  const int lane = tid & 63, half = lane >> 5, r32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int N = p.N;
   int64_t head, kblk;
   fwd_work_item(blockIdx.x, p.n_heads, n_kblk, kNone, &head, &kblk);
   const int k0 = static_cast<int>(kblk) * BK;
-  const size_t hoff = static_cast<size_t>(head) * N * D;
-  const char* Qh = reinterpret_cast<const char*>(p.Q) + hoff * 2;
-  const char* Kh = reinterpret_cast<const char*>(p.K) + hoff * 2;
-  const char* Vh = reinterpret_cast<const char*>(p.V) + hoff * 2;
-  const char* dOh = reinterpret_cast<const char*>(p.dO) + hoff * 2;
-  const float* lse_h = p.lse + static_cast<size_t>(head) * N;
-  const float* D_h = p.Dsum + static_cast<size_t>(head) * N;
+  const size_t hoff = static_cast<size_t>(head) * N * D * 2;
+  const uint32_t head_bytes = static_cast<uint32_t>(N) * ROWB;
+  const auto rQ = make_rsrc(reinterpret_cast<const char*>(p.Q) + hoff, head_bytes);
+  const auto rK = make_rsrc(reinterpret_cast<const char*>(p.K) + hoff, head_bytes);
+  const auto rV = make_rsrc(reinterpret_cast<const char*>(p.V) + hoff, head_bytes);
+  const auto rG = make_rsrc(reinterpret_cast<const char*>(p.dO) + hoff, head_bytes);
+  const auto rL = make_rsrc(p.lse + static_cast<size_t>(head) * N, static_cast<uint32_t>(N) * 4);
+  const auto rD = make_rsrc(p.Dsum + static_cast<size_t>(head) * N, static_cast<uint32_t>(N) * 4);
 
+  // K (with a negative scale's sign flip folded in) and V as B operands of
+  // S = Q K^T and dP = dO V^T: lane (key r32, half).
   const int wk0 = k0 + wave * 32;
   const int kcol = wk0 + r32;
   u32x4_t kf[KSTEPS], vf[KSTEPS];
 #pragma unroll
   for (int kk = 0; kk < KSTEPS; ++kk) {
-    const size_t off = (static_cast<size_t>(kcol) * D + kk * 16 + half * 8) * 2;
-    kf[kk] = kcol < N ? ld_global16(Kh + off) : u32x4_t{0, 0, 0, 0};
-    vf[kk] = kcol < N ? ld_global16(Vh + off) : u32x4_t{0, 0, 0, 0};
+    const uint32_t off = static_cast<uint32_t>(kcol) * ROWB + kk * 32 + half * 16;
+    kf[kk] = buf_load16(rK, off, 0) ^ p.qsign;
+    vf[kk] = buf_load16(rV, off, 0);
   }
   const float c = p.c;
 
+  // dV^T and dK^T accumulate in AGPRs (inline-asm matrix instructions); the
+  // score and dP tiles stay in VGPRs where the vector code reads them.
   f32x16_t dv[DBLK], dk[DBLK];
 #pragma unroll
   for (int b = 0; b < DBLK; ++b) {
     dv[b] = f32x16_t{};
     dk[b] = f32x16_t{};
   }
+  acc_fence(dv);
+  acc_fence(dk);
 
-  int64_t lo, hi;
-  q_tile_range(N, k0, BK, BQ, MASK, p.wl, p.wr, &lo, &hi);
-  const bool loader = tid < L::LOADERS;
-  const int rg = tid / NCH, ch = tid % NCH;
+  int64_t lo64, hi64;
+  q_tile_range(N, k0, BK, BQ, MASK, p.wl, p.wr, &lo64, &hi64);
+  const int lo = static_cast<int>(lo64), hi = static_cast<int>(hi64);
+  const TileLoader<D, NW> ld(wave, lane);
+  const TileReaders<D> rd(lane);
 
-  for (int t = static_cast<int>(lo); t < static_cast<int>(hi); ++t) {
+  // lse (in log2 units after the multiply below) and D of a query tile, one
+  // 4-byte direct load each (wavefront 0; rows past N read as zero and are
+  // masked).
+  auto load_stats = [&](int q0, float* sl, float* sd) {
+    if (wave == 0) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rL, (__attribute__((address_space(3))) void*)(sl), 4,
+                                               lane * 4, q0 * 4, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rD, (__attribute__((address_space(3))) void*)(sd), 4,
+                                               lane * 4, q0 * 4, 0, 0);
+    }
+  };
+
+  // One query tile: 32 queries at a time, S and dP, then P and dS, then the
+  // two 16-query steps of dV^T += dO^T P and dK^T += Q^T dS.
+  auto tile = [&](int t, const char* qt, const char* gt, const float* sl, const float* sd) {
     const int q0 = t * BQ;
-    u32x4_t qv[4], gv[4];
-    if (loader) {
-      L::load(qv, Qh, q0, N, rg, ch, p.qsign);
-      L::load(gv, dOh, q0, N, rg, ch);
-    }
-    float lse_v = INFINITY, D_v = 0.0f;
-    if (tid < 64 && q0 + tid < N) {
-      lse_v = lse_h[q0 + tid] * kLog2e;
-      D_v = D_h[q0 + tid];
-    }
-    __syncthreads();
-    if (loader) {
-      L::store_rows(q_rows, qv, rg, ch);
-      L::store_transposed(q_tr, qv, rg, ch);
-      L::store_rows(g_rows, gv, rg, ch);
-      L::store_transposed(g_tr, gv, rg, ch);
-    }
-    if (tid < 64) {
-      lse_t[tid] = lse_v;
-      D_t[tid] = D_v;
-    }
-    __syncthreads();
-    if (tile_none_allowed(N, q0, BQ, wk0, 32, MASK, p.wl, p.wr)) continue;
+    if (MASK != kNone && tile_none_allowed(N, q0, BQ, wk0, 32, MASK, p.wl, p.wr)) return;
     const bool full = tile_all_allowed(N, q0, BQ, wk0, 32, MASK, p.wl, p.wr);
-
-    // One 32-query block at a time: S, dP -> P, dS -> two 16-query steps of
-    // dV^T += dO^T P and dK^T += Q^T dS.
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       f32x16_t s = f32x16_t{}, dp = f32x16_t{};
-      const int row = qb * 32 + r32;
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
-        s = Elem<T>::mma(ld_lds16(q_rows + L::row_off(row, kk * 2 + half)), kf[kk], s);
-        dp = Elem<T>::mma(ld_lds16(g_rows + L::row_off(row, kk * 2 + half)), vf[kk], dp);
+        s = Elem<T>::mma(rd.rows(qt, qb, kk), kf[kk], s);
+        dp = Elem<T>::mma(rd.rows(gt, qb, kk), vf[kk], dp);
       }
       uint32_t pk[8], dsk[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float pr[2], e[2];
+      for (int g4 = 0; g4 < 4; ++g4) {
+        // Rows qb*32 + g4*8 + half*4 + 0..3 of the C tile: their lse and D.
+        const int ql0 = qb * 32 + g4 * 8 + half * 4;
+        const u32x4_t lq = *reinterpret_cast<const u32x4_t*>(sl + ql0);
+        const u32x4_t dq = *reinterpret_cast<const u32x4_t*>(sd + ql0);
+        float e[4], pr[4];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int i = 2 * j + u;
-          const int ql = qb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+        for (int u = 0; u < 4; ++u) {
+          const int i = g4 * 4 + u;
           bool ok = true;
           if (!full) {
-            const int q = q0 + ql;
+            const int q = q0 + ql0 + u;
             ok = kcol < N && q < N;
             if (MASK == kCausal) ok = ok && kcol <= q;
             if (MASK == kSliding) ok = ok && kcol >= q - p.wl && kcol <= q + p.wr;
           }
-          pr[u] = ok ? fast_exp2(fmaf(s[i], c, -lse_t[ql])) : 0.0f;
-          e[u] = pr[u] * (dp[i] - D_t[ql]);
+          pr[u] = fast_exp2(fmaf(s[i], c, -__uint_as_float(lq[u]) * kLog2e));
+          if (!ok) pr[u] = 0.0f;  // a select, not a branch
+          e[u] = pr[u] * (dp[i] - __uint_as_float(dq[u]));
         }
-        pk[j] = Elem<T>::pack2(pr[0], pr[1]);
-        dsk[j] = Elem<T>::pack2(e[0], e[1]);
+        pk[g4 * 2 + 0] = Elem<T>::pack2(pr[0], pr[1]);
+        pk[g4 * 2 + 1] = Elem<T>::pack2(pr[2], pr[3]);
+        dsk[g4 * 2 + 0] = Elem<T>::pack2(e[0], e[1]);
+        dsk[g4 * 2 + 1] = Elem<T>::pack2(e[2], e[3]);
       }
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
-        const int st = qb * 2 + h2;
         const u32x4_t bp = {pk[h2 * 4 + 0], pk[h2 * 4 + 1], pk[h2 * 4 + 2], pk[h2 * 4 + 3]};
         const u32x4_t bs = {dsk[h2 * 4 + 0], dsk[h2 * 4 + 1], dsk[h2 * 4 + 2], dsk[h2 * 4 + 3]};
 #pragma unroll
         for (int db = 0; db < DBLK; ++db) {
-          const int drow = db * 32 + r32;
-          dv[db] = Elem<T>::mma(ld_lds16(g_tr + L::tr_off(drow, st * 2 + half)), bp, dv[db]);
-          dk[db] = Elem<T>::mma(ld_lds16(q_tr + L::tr_off(drow, st * 2 + half)), bs, dk[db]);
+          if (db == 0) {
+            Elem<T>::template mma_acc<true>(dv[db], rd.trans(gt, db, qb * 2 + h2), bp);
+            Elem<T>::template mma_acc<true>(dk[db], rd.trans(qt, db, qb * 2 + h2), bs);
+          } else {
+            Elem<T>::template mma_acc<false>(dv[db], rd.trans(gt, db, qb * 2 + h2), bp);
+            Elem<T>::template mma_acc<false>(dk[db], rd.trans(qt, db, qb * 2 + h2), bs);
+          }
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  ld.load(rQ, q_lds0, lo * BQ);
+  ld.load(rG, g_lds0, lo * BQ);
+  load_stats(lo * BQ, s_lse0, s_d0);
+  wait_vmem();
+  __syncthreads();
+  for (int t = lo; t < hi; t += 2) {
+    if (t + 1 < hi) {
+      ld.load(rQ, q_lds1, (t + 1) * BQ);
+      ld.load(rG, g_lds1, (t + 1) * BQ);
+      load_stats((t + 1) * BQ, s_lse1, s_d1);
+    }
+    tile(t, q_lds0, g_lds0, s_lse0, s_d0);
+    wait_vmem();
+    __syncthreads();
+    if (t + 1 >= hi) break;
+    if (t + 2 < hi) {
+      ld.load(rQ, q_lds0, (t + 2) * BQ);
+      ld.load(rG, g_lds0, (t + 2) * BQ);
+      load_stats((t + 2) * BQ, s_lse0, s_d0);
+    }
+    tile(t + 1, q_lds1, g_lds1, s_lse1, s_d1);
+    wait_vmem();
+    __syncthreads();
   }
 
-  if (kcol < N) {
-    // Q entered the products with its sign flipped for a negative scale, so
-    // dK = |scale| dS^T Q' with Q' the stored (flipped) rows.
-    const float sc = fabsf(p.scale);
-    char* dKh = reinterpret_cast<char*>(p.dK) + hoff * 2;
-    char* dVh = reinterpret_cast<char*>(p.dV) + hoff * 2;
+  // K entered the products with a negative scale's sign flip, so
+  // dK = scale * dS^T Q with the signed scale; dV = P^T dO.
+  acc_fence(dv);
+  acc_fence(dk);
+  const float sc = p.scale;
+  const auto rdK = make_rsrc(reinterpret_cast<char*>(p.dK) + hoff, head_bytes);
+  const auto rdV = make_rsrc(reinterpret_cast<char*>(p.dV) + hoff, head_bytes);
 #pragma unroll
-    for (int db = 0; db < DBLK; ++db)
+  for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const size_t off = (static_cast<size_t>(kcol) * D + db * 32 + g * 8 + half * 4) * 2;
-        const u32x2_t a = {Elem<T>::pack2(dk[db][g * 4 + 0] * sc, dk[db][g * 4 + 1] * sc),
-                           Elem<T>::pack2(dk[db][g * 4 + 2] * sc, dk[db][g * 4 + 3] * sc)};
-        const u32x2_t b = {Elem<T>::pack2(dv[db][g * 4 + 0], dv[db][g * 4 + 1]),
-                           Elem<T>::pack2(dv[db][g * 4 + 2], dv[db][g * 4 + 3])};
-        st_global8(dKh + off, a);
-        st_global8(dVh + off, b);
-      }
-  }
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t off = static_cast<uint32_t>(kcol) * ROWB + (db * 32 + g * 8 + half * 4) * 2;
+      const u32x2_t a = {Elem<T>::pack2(dk[db][g * 4 + 0] * sc, dk[db][g * 4 + 1] * sc),
+                         Elem<T>::pack2(dk[db][g * 4 + 2] * sc, dk[db][g * 4 + 3] * sc)};
+      const u32x2_t b = {Elem<T>::pack2(dv[db][g * 4 + 0], dv[db][g * 4 + 1]),
+                         Elem<T>::pack2(dv[db][g * 4 + 2], dv[db][g * 4 + 3])};
+      buf_store8(a, rdK, off);
+      buf_store8(b, rdV, off);
+    }
 }
 
 template <typename T, int D, int MASK>
@@ -371,14 +463,14 @@ hipError_t launch_all(const BwdParams& p, hipStream_t stream) {
   const int n_qblk = static_cast<int>(ceil_div(p.N, kBwdDqBlockQ));
   hipLaunchKernelGGL((bwd_dq_kernel<T, D, MASK>),
                      dim3(static_cast<unsigned>(static_cast<int64_t>(p.n_heads) * n_qblk)),
-                     dim3(kBwdThreads), 3 * 64 * D * 2, stream, p, n_qblk);
+                     dim3(kBwdThreads), 0, stream, p, n_qblk);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
   const int n_kblk = static_cast<int>(ceil_div(p.N, kBwdKvBlockK));
   hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, MASK>),
                      dim3(static_cast<unsigned>(static_cast<int64_t>(p.n_heads) * n_kblk)),
-                     dim3(kBwdThreads), 4 * 64 * D * 2 + 2 * 64 * 4, stream, p, n_kblk);
+                     dim3(kBwdThreads), 0, stream, p, n_kblk);
   return hipGetLastError();
 }
 

@@ -45,6 +45,15 @@ struct Elem<__bf16> {
     f32x2_t v = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
   }
+  // c += a * b with the accumulator in AGPRs (see acc_fence); NOP waits the
+  // two cycles a matrix instruction needs after vector code wrote b.
+  template <bool NOP>
+  static __device__ __forceinline__ void mma_acc(f32x16_t& c, u32x4_t a, u32x4_t b) {
+    if (NOP)
+      asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+    else
+      asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  }
   // acc + lo + hi of a packed pair, exactly as stored (v_dot2 with ones).
   static __device__ __forceinline__ float add_pair(uint32_t packed, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, packed),
@@ -62,11 +71,30 @@ struct Elem<_Float16> {
     f32x2_t v = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2_t));
   }
+  template <bool NOP>
+  static __device__ __forceinline__ void mma_acc(f32x16_t& c, u32x4_t a, u32x4_t b) {
+    if (NOP)
+      asm("s_nop 1\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+    else
+      asm("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  }
   static __device__ __forceinline__ float add_pair(uint32_t packed, float acc) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, packed),
                                   __builtin_bit_cast(f16x2_t, 0x3C003C00u), acc, false);
   }
 };
+
+// Accumulators held in AGPRs by the inline-asm matrix instructions of
+// mma_acc: the compiler does not see those instructions, so before vector
+// code reads or rewrites such accumulators this fence waits out the matrix
+// pipeline (an 8-pass 32x32 product needs well under 24 wait states) and
+// ties every accumulator to it, so that no such access is scheduled earlier.
+template <int N>
+__device__ __forceinline__ void acc_fence(f32x16_t (&acc)[N]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+  for (int b = 0; b < N; ++b) asm volatile("" : "+a"(acc[b]));
+}
 
 // Position of reduction index j inside its group of 16 in a permuted LDS
 // row: swaps bits 2 and 3 (see the file comment).
