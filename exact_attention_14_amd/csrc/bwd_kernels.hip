@@ -206,6 +206,17 @@ void bwd_dq_kernel(BwdParams p, int n_qblk) {
         s = Elem<T>::mma(rd.rows(kt, kb, kk), qf[kk], s);
         dp = Elem<T>::mma(rd.rows(vt, kb, kk), gf[kk], dp);
       }
+      // Boundary tiles only: masked scores become -inf, so P = 0 there.
+      if (!full) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+          bool ok = key < N;
+          if (MASK == kCausal) ok = ok && key <= qrow;
+          if (MASK == kSliding) ok = ok && key >= qrow - p.wl && key <= qrow + p.wr;
+          if (!ok) s[i] = -INFINITY;
+        }
+      }
       uint32_t ds[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -213,16 +224,7 @@ void bwd_dq_kernel(BwdParams p, int n_qblk) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int i = 2 * j + u;
-          bool ok = true;
-          if (!full) {
-            const int key = k0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-            ok = key < N;
-            if (MASK == kCausal) ok = ok && key <= qrow;
-            if (MASK == kSliding) ok = ok && key >= qrow - p.wl && key <= qrow + p.wr;
-          }
-          float pr = fast_exp2(fmaf(s[i], c, -lse2));
-          if (!ok) pr = 0.0f;  // a select, not a branch
-          e[u] = pr * (dp[i] - Dq);
+          e[u] = fast_exp2(fmaf(s[i], c, -lse2)) * (dp[i] - Dq);
         }
         ds[j] = Elem<T>::pack2(e[0], e[1]);
       }
@@ -333,9 +335,8 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
   const TileLoader<D, NW> ld(wave, lane);
   const TileReaders<D> rd(lane);
 
-  // lse (in log2 units after the multiply below) and D of a query tile, one
-  // 4-byte direct load each (wavefront 0; rows past N read as zero and are
-  // masked).
+  // lse and D of a query tile, one 4-byte direct load each (wavefront 0;
+  // rows past N read as zero and are masked).
   auto load_stats = [&](int q0, float* sl, float* sd) {
     if (wave == 0) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rL, (__attribute__((address_space(3))) void*)(sl), 4,
@@ -359,10 +360,22 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
         s = Elem<T>::mma(rd.rows(qt, qb, kk), kf[kk], s);
         dp = Elem<T>::mma(rd.rows(gt, qb, kk), vf[kk], dp);
       }
+      // Boundary tiles only: masked scores become -inf, so P = 0 there.
+      if (!full) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int q = q0 + qb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+          bool ok = kcol < N && q < N;
+          if (MASK == kCausal) ok = ok && kcol <= q;
+          if (MASK == kSliding) ok = ok && kcol >= q - p.wl && kcol <= q + p.wr;
+          if (!ok) s[i] = -INFINITY;
+        }
+      }
       uint32_t pk[8], dsk[8];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        // Rows qb*32 + g4*8 + half*4 + 0..3 of the C tile: their lse and D.
+        // Rows qb*32 + g4*8 + half*4 + 0..3 of the C tile: their lse (in log2
+        // units) and D.
         const int ql0 = qb * 32 + g4 * 8 + half * 4;
         const u32x4_t lq = *reinterpret_cast<const u32x4_t*>(sl + ql0);
         const u32x4_t dq = *reinterpret_cast<const u32x4_t*>(sd + ql0);
@@ -370,15 +383,7 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int i = g4 * 4 + u;
-          bool ok = true;
-          if (!full) {
-            const int q = q0 + ql0 + u;
-            ok = kcol < N && q < N;
-            if (MASK == kCausal) ok = ok && kcol <= q;
-            if (MASK == kSliding) ok = ok && kcol >= q - p.wl && kcol <= q + p.wr;
-          }
-          pr[u] = fast_exp2(fmaf(s[i], c, -__uint_as_float(lq[u]) * kLog2e));
-          if (!ok) pr[u] = 0.0f;  // a select, not a branch
+          pr[u] = fast_exp2(fmaf(s[i], c, -__uint_as_float(lq[u])));
           e[u] = pr[u] * (dp[i] - __uint_as_float(dq[u]));
         }
         pk[g4 * 2 + 0] = Elem<T>::pack2(pr[0], pr[1]);
@@ -405,10 +410,16 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
     }
   };
 
+  // The wavefront that loaded a tile's lse converts it to log2 units once
+  // its own direct load has landed (the barrier that follows publishes it).
+  auto scale_lse = [&](float* sl) {
+    if (wave == 0) sl[lane] *= kLog2e;
+  };
   ld.load(rQ, q_lds0, lo * BQ);
   ld.load(rG, g_lds0, lo * BQ);
   load_stats(lo * BQ, s_lse0, s_d0);
   wait_vmem();
+  scale_lse(s_lse0);
   __syncthreads();
   for (int t = lo; t < hi; t += 2) {
     if (t + 1 < hi) {
@@ -418,6 +429,7 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
     }
     tile(t, q_lds0, g_lds0, s_lse0, s_d0);
     wait_vmem();
+    scale_lse(s_lse1);
     __syncthreads();
     if (t + 1 >= hi) break;
     if (t + 2 < hi) {
@@ -427,6 +439,7 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
     }
     tile(t + 1, q_lds1, g_lds1, s_lse1, s_d1);
     wait_vmem();
+    scale_lse(s_lse0);
     __syncthreads();
   }
 
