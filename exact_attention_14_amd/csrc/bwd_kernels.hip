@@ -15,8 +15,9 @@
 //   3. bwd_dkdv:    key-major.  Per 64-query tile, 32 queries at a time:
 //                   S = Q K^T, P, dP = dO V^T, dS = P (dP - D),
 //                   dV^T += dO^T P, dK^T += Q^T dS.  K and V stay in
-//                   registers; one wavefront per SIMD (the four accumulator
-//                   sets do not fit two).
+//                   registers; each wavefront owns 64 keys (two blocks that
+//                   share every operand read from LDS) with its dV and dK
+//                   accumulators in AGPRs, one wavefront per SIMD.
 // Tiles stream through double-buffered LDS stages filled by direct
 // HBM-to-LDS loads (one array per stage, so reading one stage never waits
 // for the loads into the other).  Each 64-row tile is stored once, row-major
@@ -277,12 +278,15 @@ void bwd_dq_kernel(BwdParams p, int n_qblk) {
 }
 
 // ---------------------------------------------------------------- dK, dV
+// Each wavefront owns KB = 2 blocks of 32 keys, so every Q / dO operand read
+// from LDS feeds the products of both blocks.
 template <typename T, int D, int MASK>
 __global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
   using L = BwdTile<D>;
   constexpr int BK = kBwdKvBlockK, BQ = kBwdKvBlockQ, NW = kBwdThreads / 64;
-  static_assert(BQ == 64 && BK == 32 * NW, "dK/dV tile geometry");
+  constexpr int KB = BK / (32 * NW);
+  static_assert(BQ == 64 && KB == 2, "dK/dV tile geometry");
   constexpr int KSTEPS = D / 16, DBLK = D / 32;
   constexpr uint32_t ROWB = L::ROWB;
   __shared__ __attribute__((aligned(16))) char q_lds0[L::BYTES], q_lds1[L::BYTES];
@@ -306,23 +310,27 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
   const auto rD = make_rsrc(p.Dsum + static_cast<size_t>(head) * N, static_cast<uint32_t>(N) * 4);
 
   // K (with a negative scale's sign flip folded in) and V as B operands of
-  // S = Q K^T and dP = dO V^T: lane (key r32, half).
-  const int wk0 = k0 + wave * 32;
-  const int kcol = wk0 + r32;
-  u32x4_t kf[KSTEPS], vf[KSTEPS];
+  // S = Q K^T and dP = dO V^T: lane (key r32 of block kb, half).
+  const int wk0 = k0 + wave * 32 * KB;
+  int kcol[KB];
+  u32x4_t kf[KB][KSTEPS], vf[KB][KSTEPS];
 #pragma unroll
-  for (int kk = 0; kk < KSTEPS; ++kk) {
-    const uint32_t off = static_cast<uint32_t>(kcol) * ROWB + kk * 32 + half * 16;
-    kf[kk] = buf_load16(rK, off, 0) ^ p.qsign;
-    vf[kk] = buf_load16(rV, off, 0);
+  for (int kb = 0; kb < KB; ++kb) {
+    kcol[kb] = wk0 + kb * 32 + r32;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      const uint32_t off = static_cast<uint32_t>(kcol[kb]) * ROWB + kk * 32 + half * 16;
+      kf[kb][kk] = buf_load16(rK, off, 0) ^ p.qsign;
+      vf[kb][kk] = buf_load16(rV, off, 0);
+    }
   }
   const float c = p.c;
 
   // dV^T and dK^T accumulate in AGPRs (inline-asm matrix instructions); the
   // score and dP tiles stay in VGPRs where the vector code reads them.
-  f32x16_t dv[DBLK], dk[DBLK];
+  f32x16_t dv[KB * DBLK], dk[KB * DBLK];
 #pragma unroll
-  for (int b = 0; b < DBLK; ++b) {
+  for (int b = 0; b < KB * DBLK; ++b) {
     dv[b] = f32x16_t{};
     dk[b] = f32x16_t{};
   }
@@ -346,63 +354,88 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
     }
   };
 
-  // One query tile: 32 queries at a time, S and dP, then P and dS, then the
-  // two 16-query steps of dV^T += dO^T P and dK^T += Q^T dS.
+  // One query tile: 32 queries at a time, S and dP for both key blocks, then
+  // P and dS, then the two 16-query steps of dV^T += dO^T P and
+  // dK^T += Q^T dS.
   auto tile = [&](int t, const char* qt, const char* gt, const float* sl, const float* sd) {
     const int q0 = t * BQ;
-    if (MASK != kNone && tile_none_allowed(N, q0, BQ, wk0, 32, MASK, p.wl, p.wr)) return;
-    const bool full = tile_all_allowed(N, q0, BQ, wk0, 32, MASK, p.wl, p.wr);
+    if (MASK != kNone && tile_none_allowed(N, q0, BQ, wk0, 32 * KB, MASK, p.wl, p.wr)) return;
+    const bool full = tile_all_allowed(N, q0, BQ, wk0, 32 * KB, MASK, p.wl, p.wr);
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      f32x16_t s = f32x16_t{}, dp = f32x16_t{};
+      f32x16_t s[KB], dp[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        s[kb] = f32x16_t{};
+        dp[kb] = f32x16_t{};
+      }
 #pragma unroll
       for (int kk = 0; kk < KSTEPS; ++kk) {
-        s = Elem<T>::mma(rd.rows(qt, qb, kk), kf[kk], s);
-        dp = Elem<T>::mma(rd.rows(gt, qb, kk), vf[kk], dp);
+        const u32x4_t aq = rd.rows(qt, qb, kk), ag = rd.rows(gt, qb, kk);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          s[kb] = Elem<T>::mma(aq, kf[kb][kk], s[kb]);
+          dp[kb] = Elem<T>::mma(ag, vf[kb][kk], dp[kb]);
+        }
       }
       // Boundary tiles only: masked scores become -inf, so P = 0 there.
       if (!full) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int q = q0 + qb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
-          bool ok = kcol < N && q < N;
-          if (MASK == kCausal) ok = ok && kcol <= q;
-          if (MASK == kSliding) ok = ok && kcol >= q - p.wl && kcol <= q + p.wr;
-          if (!ok) s[i] = -INFINITY;
-        }
+        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int q = q0 + qb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
+            bool ok = kcol[kb] < N && q < N;
+            if (MASK == kCausal) ok = ok && kcol[kb] <= q;
+            if (MASK == kSliding) ok = ok && kcol[kb] >= q - p.wl && kcol[kb] <= q + p.wr;
+            if (!ok) s[kb][i] = -INFINITY;
+          }
       }
-      uint32_t pk[8], dsk[8];
+      uint32_t pk[KB][8], dsk[KB][8];
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
-        // Rows qb*32 + g4*8 + half*4 + 0..3 of the C tile: their lse (in log2
+        // Rows qb*32 + g4*8 + half*4 + 0..3 of the C tiles: their lse (in log2
         // units) and D.
         const int ql0 = qb * 32 + g4 * 8 + half * 4;
         const u32x4_t lq = *reinterpret_cast<const u32x4_t*>(sl + ql0);
         const u32x4_t dq = *reinterpret_cast<const u32x4_t*>(sd + ql0);
-        float e[4], pr[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = g4 * 4 + u;
-          pr[u] = fast_exp2(fmaf(s[i], c, -__uint_as_float(lq[u])));
-          e[u] = pr[u] * (dp[i] - __uint_as_float(dq[u]));
+        for (int kb = 0; kb < KB; ++kb) {
+          float e[4], pr[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int i = g4 * 4 + u;
+            pr[u] = fast_exp2(fmaf(s[kb][i], c, -__uint_as_float(lq[u])));
+            e[u] = pr[u] * (dp[kb][i] - __uint_as_float(dq[u]));
+          }
+          pk[kb][g4 * 2 + 0] = Elem<T>::pack2(pr[0], pr[1]);
+          pk[kb][g4 * 2 + 1] = Elem<T>::pack2(pr[2], pr[3]);
+          dsk[kb][g4 * 2 + 0] = Elem<T>::pack2(e[0], e[1]);
+          dsk[kb][g4 * 2 + 1] = Elem<T>::pack2(e[2], e[3]);
         }
-        pk[g4 * 2 + 0] = Elem<T>::pack2(pr[0], pr[1]);
-        pk[g4 * 2 + 1] = Elem<T>::pack2(pr[2], pr[3]);
-        dsk[g4 * 2 + 0] = Elem<T>::pack2(e[0], e[1]);
-        dsk[g4 * 2 + 1] = Elem<T>::pack2(e[2], e[3]);
       }
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
-        const u32x4_t bp = {pk[h2 * 4 + 0], pk[h2 * 4 + 1], pk[h2 * 4 + 2], pk[h2 * 4 + 3]};
-        const u32x4_t bs = {dsk[h2 * 4 + 0], dsk[h2 * 4 + 1], dsk[h2 * 4 + 2], dsk[h2 * 4 + 3]};
+        u32x4_t bp[KB], bs[KB];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          bp[kb] = u32x4_t{pk[kb][h2 * 4 + 0], pk[kb][h2 * 4 + 1], pk[kb][h2 * 4 + 2],
+                           pk[kb][h2 * 4 + 3]};
+          bs[kb] = u32x4_t{dsk[kb][h2 * 4 + 0], dsk[kb][h2 * 4 + 1], dsk[kb][h2 * 4 + 2],
+                           dsk[kb][h2 * 4 + 3]};
+        }
 #pragma unroll
         for (int db = 0; db < DBLK; ++db) {
-          if (db == 0) {
-            Elem<T>::template mma_acc<true>(dv[db], rd.trans(gt, db, qb * 2 + h2), bp);
-            Elem<T>::template mma_acc<true>(dk[db], rd.trans(qt, db, qb * 2 + h2), bs);
-          } else {
-            Elem<T>::template mma_acc<false>(dv[db], rd.trans(gt, db, qb * 2 + h2), bp);
-            Elem<T>::template mma_acc<false>(dk[db], rd.trans(qt, db, qb * 2 + h2), bs);
+          const u32x4_t ag = rd.trans(gt, db, qb * 2 + h2), aq = rd.trans(qt, db, qb * 2 + h2);
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            if (db == 0) {
+              Elem<T>::template mma_acc<true>(dv[kb * DBLK + db], ag, bp[kb]);
+              Elem<T>::template mma_acc<true>(dk[kb * DBLK + db], aq, bs[kb]);
+            } else {
+              Elem<T>::template mma_acc<false>(dv[kb * DBLK + db], ag, bp[kb]);
+              Elem<T>::template mma_acc<false>(dk[kb * DBLK + db], aq, bs[kb]);
+            }
           }
         }
       }
@@ -451,17 +484,22 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
   const auto rdK = make_rsrc(reinterpret_cast<char*>(p.dK) + hoff, head_bytes);
   const auto rdV = make_rsrc(reinterpret_cast<char*>(p.dV) + hoff, head_bytes);
 #pragma unroll
-  for (int db = 0; db < DBLK; ++db)
+  for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const uint32_t off = static_cast<uint32_t>(kcol) * ROWB + (db * 32 + g * 8 + half * 4) * 2;
-      const u32x2_t a = {Elem<T>::pack2(dk[db][g * 4 + 0] * sc, dk[db][g * 4 + 1] * sc),
-                         Elem<T>::pack2(dk[db][g * 4 + 2] * sc, dk[db][g * 4 + 3] * sc)};
-      const u32x2_t b = {Elem<T>::pack2(dv[db][g * 4 + 0], dv[db][g * 4 + 1]),
-                         Elem<T>::pack2(dv[db][g * 4 + 2], dv[db][g * 4 + 3])};
-      buf_store8(a, rdK, off);
-      buf_store8(b, rdV, off);
-    }
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x16_t& a_ = dk[kb * DBLK + db];
+        const f32x16_t& b_ = dv[kb * DBLK + db];
+        const uint32_t off =
+            static_cast<uint32_t>(kcol[kb]) * ROWB + (db * 32 + g * 8 + half * 4) * 2;
+        const u32x2_t a = {Elem<T>::pack2(a_[g * 4 + 0] * sc, a_[g * 4 + 1] * sc),
+                           Elem<T>::pack2(a_[g * 4 + 2] * sc, a_[g * 4 + 3] * sc)};
+        const u32x2_t b = {Elem<T>::pack2(b_[g * 4 + 0], b_[g * 4 + 1]),
+                           Elem<T>::pack2(b_[g * 4 + 2], b_[g * 4 + 3])};
+        buf_store8(a, rdK, off);
+        buf_store8(b, rdV, off);
+      }
 }
 
 template <typename T, int D, int MASK>

@@ -31,10 +31,10 @@ ATTN_HD constexpr int fwd_waves(int mode) { return mode == 0 ? 8 : 4; }
 ATTN_HD constexpr int fwd_block_q(int mode) { return 32 * fwd_waves(mode); }
 
 // Backward: the dQ pass mirrors the forward (query-major); the dK/dV pass is
-// key-major with 4 wavefronts x 32 key rows and 64-row query tiles.
+// key-major with 4 wavefronts x 64 key rows and 64-row query tiles.
 constexpr int kBwdDqBlockQ = 128;
 constexpr int kBwdDqBlockK = 64;
-constexpr int kBwdKvBlockK = 128;
+constexpr int kBwdKvBlockK = 256;
 constexpr int kBwdKvBlockQ = 64;
 constexpr int kBwdThreads = 256;
 
