@@ -297,6 +297,9 @@ void fwd_kernel(FwdParams p) {
   wait_vmem();
   __syncthreads();
   scores(k_lds0, sA);
+  // The first step refills stage 0 with K of tile lo+2: every wavefront must
+  // have read tile lo's keys from it first.
+  __syncthreads();
 
   // One pipeline step; P = (t - lo) % 2 selects the stages at compile time.
   auto step = [&](auto P_, int t, f32x16_t cur[2], f32x16_t nxt[2]) {
