@@ -9,7 +9,9 @@ device memory.  The default workload is B=4, H=32, N=4096, d=128, bf16, no
 mask.  Prints one JSON line with the throughput in TFLOP/s of algorithmic work
 (4*d FLOP per allowed (query, key) pair), the roofline position of the forward
 kernel (HIP events on the launch stream), and the fp64 CPU oracle timed on a
-bounded sample of the same workload.
+bounded sample of the same workload.  For the workload with an upstream
+gradient (the fp16 causal forward + backward), the recomputation backward is
+timed as well and reported in a "backward" object of the same line.
 """
 from __future__ import annotations
 
@@ -138,6 +140,37 @@ def main():
     achieved = flops / (ms_kernel * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
 
+    # The recomputation backward, for workloads that carry an upstream
+    # gradient: timed the same way, from the O and lse of the forward above.
+    backward = None
+    if w.backward:
+        do = inp["do"].to("cuda")
+        ws = torch.empty(max(ea.attn_bwd_workspace_bytes(q.dtype, w.B, w.H, w.N, w.d), 16),
+                         dtype=torch.uint8, device="cuda")
+
+        def bstep():
+            ea.attn_bwd(q, k, v, o, lse, do, mask=mask, scale=w.scale, workspace=ws)
+
+        for _ in range(args.warmup):
+            bstep()
+        torch.cuda.synchronize()
+        tb0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            bstep()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        tb1 = time.perf_counter()
+        b_ms = ev0.elapsed_time(ev1) / args.steps
+        bflops = 10 * w.d * w.B * w.H * allowed_pairs(w.N, w.mask, w.window_left, w.window_right)
+        backward = {"ms_per_call": round((tb1 - tb0) * 1e3 / args.steps, 5),
+                    "kernel_ms": round(b_ms, 5),
+                    "tflops": round(bflops / (b_ms * 1e-3) / 1e12, 3),
+                    "frac_of_peak": round(bflops / (b_ms * 1e-3) / 1e12 / PEAK_TFLOPS[w.dtype], 4),
+                    "flop_per_call": bflops,
+                    "flop_model": "10*d per allowed pair (S, dP, dV, dK, dQ products)"}
+        del do, ws
+
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -181,6 +214,8 @@ def main():
                      "kernel": "fwd_kernel", "kernel_ms": round(ms_kernel, 5),
                      "flop_per_launch": flops},
     }
+    if backward is not None:
+        rec["backward"] = backward
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(rec), flush=True)

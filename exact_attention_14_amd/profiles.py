@@ -12,9 +12,10 @@ counters by what the same counters read for the calibration copy of M MiB
 (a device-to-device copy reads and writes exactly M MiB), giving HBM bytes
 per launch.  The JSON records a hash of the forward kernel's sources so that
 bench.py reports the traffic only while the kernel is unchanged.  ``counters``
-summarises one ``--pmc`` pass over the forward (per-dispatch means) and
-derives its clock and matrix-core busy fraction: GRBM_GUI_ACTIVE is summed
-over the 8 dies and SQ_VALU_MFMA_BUSY_CYCLES over the 1024 SIMDs.
+summarises one ``--pmc`` pass (per-dispatch means of every attention kernel
+in it) and derives each kernel's clock and matrix-core busy fraction:
+GRBM_GUI_ACTIVE is summed over the 8 dies and SQ_VALU_MFMA_BUSY_CYCLES over
+the 1024 SIMDs.
 """
 from __future__ import annotations
 
@@ -105,28 +106,42 @@ def traffic(fetch_dir: str, write_dir: str, workload: str, copy_mib: int, out_js
 
 
 def counters(counter_dir: str, kernel_stats: str, out_md: str, command: str) -> None:
-    per = {}
+    keys = ("fwd_kernel", "bwd_rowdot_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel")
+    per = {}  # kernel -> counter -> dispatch -> value
     for path in glob.glob(os.path.join(counter_dir, "*counter_collection.csv")):
         for r in csv.DictReader(open(path)):
-            if "fwd_kernel" not in r["Kernel_Name"]:
+            key = next((k for k in keys if k in r["Kernel_Name"]), None)
+            if key is None:
                 continue
-            per.setdefault(r["Counter_Name"], {}).setdefault(r["Dispatch_Id"], 0.0)
-            per[r["Counter_Name"]][r["Dispatch_Id"]] += float(r["Counter_Value"])
-    mean = {k: sum(v.values()) / len(v) for k, v in per.items()}
-    avg_ns = [float(r["AverageNs"]) for r in csv.DictReader(open(kernel_stats))
-              if "fwd_kernel" in r["Name"]][0]
-    lines = ["# Forward kernel counters (rocprofv3 PMC)", "", f"Command: `{command}`", "",
-             f"Kernel duration (average from the kernel trace of the same workload): "
-             f"{avg_ns / 1e3:.1f} us", "", "| counter | mean per dispatch |", "|---|---|"]
-    lines += [f"| {k} | {v:.4g} |" for k, v in sorted(mean.items())]
-    if "GRBM_GUI_ACTIVE" in mean:
-        cycles = mean["GRBM_GUI_ACTIVE"] / 8
-        lines += ["", f"- cycles per die: {cycles:.4g}; clock = cycles / duration = "
-                      f"{cycles / avg_ns:.2f} GHz"]
-        if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
-            lines.append(f"- matrix cores busy: {mean['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024 / cycles:.1%}"
-                         " of cycles (per SIMD)")
-    lines.append("")
+            d = per.setdefault(key, {}).setdefault(r["Counter_Name"], {})
+            d[r["Dispatch_Id"]] = d.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    durations = {}
+    for r in csv.DictReader(open(kernel_stats)):
+        key = next((k for k in keys if k in r["Name"]), None)
+        if key is not None:
+            durations[key] = float(r["AverageNs"])
+    lines = ["# Kernel counters (rocprofv3 PMC)", "", f"Command: `{command}`", "",
+             "Means per dispatch; durations are the averages from the kernel trace of the same",
+             "workload.  GRBM_GUI_ACTIVE is summed over the 8 dies, SQ_VALU_MFMA_BUSY_CYCLES over",
+             "the 1024 SIMDs.", ""]
+    for key in keys:
+        if key not in per:
+            continue
+        mean = {k: sum(v.values()) / len(v) for k, v in per[key].items()}
+        lines += [f"## {key}", ""]
+        if key in durations:
+            lines += [f"Kernel duration: {durations[key] / 1e3:.1f} us", ""]
+        lines += ["| counter | mean per dispatch |", "|---|---|"]
+        lines += [f"| {k} | {v:.4g} |" for k, v in sorted(mean.items())]
+        if "GRBM_GUI_ACTIVE" in mean and key in durations:
+            cycles = mean["GRBM_GUI_ACTIVE"] / 8
+            lines += ["", f"- cycles per die: {cycles:.4g}; clock = cycles / duration = "
+                          f"{cycles / durations[key]:.2f} GHz"]
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+                lines.append(f"- matrix cores busy: "
+                             f"{mean['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024 / cycles:.1%} of cycles "
+                             "(per SIMD)")
+        lines.append("")
     with open(out_md, "w") as f:
         f.write("\n".join(lines))
 
