@@ -13,7 +13,9 @@
 //                   dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.  Q and dO stay
 //                   in registers; two wavefronts per SIMD.
 //   3. bwd_dkdv:    key-major.  Per 64-query tile, 32 queries at a time:
-//                   S = Q K^T, P, dP = dO V^T, dS = P (dP - D),
+//                   S = Q K^T, P, dP = dO V^T, dS = P (dP - D) (the
+//                   offsets lse and D enter as the accumulators' starting
+//                   values),
 //                   dV^T += dO^T P, dK^T += Q^T dS.  K and V stay in
 //                   registers; each wavefront owns 64 keys (two blocks that
 //                   share every operand read from LDS) with its dV and dK
@@ -344,7 +346,9 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
   const TileReaders<D> rd(lane);
 
   // lse and D of a query tile, one 4-byte direct load each (wavefront 0;
-  // rows past N read as zero and are masked).
+  // rows past N read as zero and are masked).  Once landed they are turned
+  // into the starting values of the score and dP accumulators:
+  // -lse * log2(e) / c and -D.
   auto load_stats = [&](int q0, float* sl, float* sd) {
     if (wave == 0) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rL, (__attribute__((address_space(3))) void*)(sl), 4,
@@ -354,9 +358,23 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
     }
   };
 
-  // One query tile: 32 queries at a time, S and dP for both key blocks, then
-  // P and dS, then the two 16-query steps of dV^T += dO^T P and
-  // dK^T += Q^T dS.
+  // 32 per-row values of a query block in the layout of the score tile's
+  // rows: element 4*g4 + u of a lane is row g4*8 + half*4 + u.
+  auto row_tile = [&](const float* v, int qb) {
+    f32x16_t t;
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const u32x4_t x = *reinterpret_cast<const u32x4_t*>(v + qb * 32 + g4 * 8 + half * 4);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) t[g4 * 4 + u] = __uint_as_float(x[u]);
+    }
+    return t;
+  };
+
+  // One query tile: 32 queries at a time, S and dP for both key blocks (the
+  // accumulators start from -lse * log2(e) / c and -D, so the products
+  // deliver exp2's argument divided by c and dP - D), then P and dS, then the
+  // two 16-query steps of dV^T += dO^T P and dK^T += Q^T dS.
   auto tile = [&](int t, const char* qt, const char* gt, const float* sl, const float* sd) {
     const int q0 = t * BQ;
     if (MASK != kNone && tile_none_allowed(N, q0, BQ, wk0, 32 * KB, MASK, p.wl, p.wr)) return;
@@ -364,13 +382,17 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
       f32x16_t s[KB], dp[KB];
+      {
+        const f32x16_t lt = row_tile(sl, qb), dt = row_tile(sd, qb);
+        const u32x4_t aq = rd.rows(qt, qb, 0), ag = rd.rows(gt, qb, 0);
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        s[kb] = f32x16_t{};
-        dp[kb] = f32x16_t{};
+        for (int kb = 0; kb < KB; ++kb) {
+          s[kb] = Elem<T>::mma(aq, kf[kb][0], lt);
+          dp[kb] = Elem<T>::mma(ag, vf[kb][0], dt);
+        }
       }
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
+      for (int kk = 1; kk < KSTEPS; ++kk) {
         const u32x4_t aq = rd.rows(qt, qb, kk), ag = rd.rows(gt, qb, kk);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
@@ -393,27 +415,13 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
       }
       uint32_t pk[KB][8], dsk[KB][8];
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        // Rows qb*32 + g4*8 + half*4 + 0..3 of the C tiles: their lse (in log2
-        // units) and D.
-        const int ql0 = qb * 32 + g4 * 8 + half * 4;
-        const u32x4_t lq = *reinterpret_cast<const u32x4_t*>(sl + ql0);
-        const u32x4_t dq = *reinterpret_cast<const u32x4_t*>(sd + ql0);
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          float e[4], pr[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int i = g4 * 4 + u;
-            pr[u] = fast_exp2(fmaf(s[kb][i], c, -__uint_as_float(lq[u])));
-            e[u] = pr[u] * (dp[kb][i] - __uint_as_float(dq[u]));
-          }
-          pk[kb][g4 * 2 + 0] = Elem<T>::pack2(pr[0], pr[1]);
-          pk[kb][g4 * 2 + 1] = Elem<T>::pack2(pr[2], pr[3]);
-          dsk[kb][g4 * 2 + 0] = Elem<T>::pack2(e[0], e[1]);
-          dsk[kb][g4 * 2 + 1] = Elem<T>::pack2(e[2], e[3]);
+        for (int j = 0; j < 8; ++j) {
+          const float p0 = fast_exp2(s[kb][2 * j] * c), p1 = fast_exp2(s[kb][2 * j + 1] * c);
+          pk[kb][j] = Elem<T>::pack2(p0, p1);
+          dsk[kb][j] = Elem<T>::pack2(p0 * dp[kb][2 * j], p1 * dp[kb][2 * j + 1]);
         }
-      }
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         u32x4_t bp[KB], bs[KB];
@@ -443,16 +451,19 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
     }
   };
 
-  // The wavefront that loaded a tile's lse converts it to log2 units once
-  // its own direct load has landed (the barrier that follows publishes it).
-  auto scale_lse = [&](float* sl) {
-    if (wave == 0) sl[lane] *= kLog2e;
+  // The wavefront that loaded a tile's statistics converts them once its own
+  // direct loads have landed (the barrier that follows publishes them).
+  auto convert_stats = [&](float* sl, float* sd) {
+    if (wave == 0) {
+      sl[lane] *= p.lse_mul;
+      sd[lane] = -sd[lane];
+    }
   };
   ld.load(rQ, q_lds0, lo * BQ);
   ld.load(rG, g_lds0, lo * BQ);
   load_stats(lo * BQ, s_lse0, s_d0);
   wait_vmem();
-  scale_lse(s_lse0);
+  convert_stats(s_lse0, s_d0);
   __syncthreads();
   for (int t = lo; t < hi; t += 2) {
     if (t + 1 < hi) {
@@ -462,7 +473,7 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
     }
     tile(t, q_lds0, g_lds0, s_lse0, s_d0);
     wait_vmem();
-    scale_lse(s_lse1);
+    convert_stats(s_lse1, s_d1);
     __syncthreads();
     if (t + 1 >= hi) break;
     if (t + 2 < hi) {
@@ -472,7 +483,7 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
     }
     tile(t + 1, q_lds1, g_lds1, s_lse1, s_d1);
     wait_vmem();
-    scale_lse(s_lse0);
+    convert_stats(s_lse0, s_d0);
     __syncthreads();
   }
 

@@ -37,6 +37,7 @@ struct BwdParams {
   float c;        // |scale| * log2(e), at least 1e-30
   float scale;    // the signed scale (applied to dQ and dK)
   uint32_t qsign; // sign flip folded into Q for negative scales
+  float lse_mul;  // -log2(e) / c: lse * lse_mul is a row's offset in score units
 };
 
 hipError_t launch_fwd(const FwdParams& p, int dt_bf16, int d, int mode, int64_t n_wg,

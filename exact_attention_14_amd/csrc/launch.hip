@@ -70,6 +70,7 @@ attn_status attn_bwd(attn_dtype dt, const void* Q, const void* K, const void* V,
   p.c = attn::exp2_coeff(scale);
   p.scale = scale;
   p.qsign = scale < 0.0f ? 0x80008000u : 0u;
+  p.lse_mul = -1.4426950408889634f / p.c;
   hipError_t e = attn::launch_bwd(p, dt == ATTN_BF16, static_cast<int>(d), mode,
                                   static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
