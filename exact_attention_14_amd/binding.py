@@ -26,7 +26,7 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_E_NULLPTR", 2: "ATTN_E_SHAPE", 3: "ATTN_E_UNSUP
 # Every symbol include/attn.h declares.
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str",
            "attn_fwd_check", "attn_bwd_check", "attn_fwd_tiles", "attn_kv_tile_range",
-           "attn_fwd_workgroup")
+           "attn_fwd_workgroup", "attn_bwd_kv_workgroup")
 
 
 class AttnError(RuntimeError):
@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
     L.attn_kv_tile_range.restype = i32
     L.attn_fwd_workgroup.argtypes = [i64, i64, i64, i32, p64, p64]
     L.attn_fwd_workgroup.restype = i32
+    L.attn_bwd_kv_workgroup.argtypes = [i64, i64, i64, i32, p64, p64]
+    L.attn_bwd_kv_workgroup.restype = i32
     _lib = L
     return L
 
@@ -196,3 +198,10 @@ def attn_fwd_workgroup(wg, n_heads, n_qblk, mode):
     st = lib().attn_fwd_workgroup(wg, n_heads, n_qblk, mode, ctypes.byref(h), ctypes.byref(qb))
     _raise("attn_fwd_workgroup", st)
     return h.value, qb.value
+
+
+def attn_bwd_kv_workgroup(wg, n_heads, n_kblk, mode):
+    h, kb = ctypes.c_int64(), ctypes.c_int64()
+    st = lib().attn_bwd_kv_workgroup(wg, n_heads, n_kblk, mode, ctypes.byref(h), ctypes.byref(kb))
+    _raise("attn_bwd_kv_workgroup", st)
+    return h.value, kb.value

@@ -300,7 +300,7 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int N = p.N;
   int64_t head, kblk;
-  fwd_work_item(blockIdx.x, p.n_heads, n_kblk, kNone, &head, &kblk);
+  kv_work_item(blockIdx.x, p.n_heads, n_kblk, MASK, &head, &kblk);
   const int k0 = static_cast<int>(kblk) * BK;
   const size_t hoff = static_cast<size_t>(head) * N * D * 2;
   const uint32_t head_bytes = static_cast<uint32_t>(N) * ROWB;

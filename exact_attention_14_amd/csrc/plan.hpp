@@ -134,4 +134,23 @@ ATTN_HD void fwd_work_item(int64_t wg, int64_t n_heads, int64_t n_qblk, int mode
   *qblk = (mode == kCausal) ? (n_qblk - 1 - qb) : qb;
 }
 
+// Work item -> (head, key block) of the backward's key-major pass.  Under a
+// causal mask key block b sees every query tile from b on, so block 0 does
+// up to 16 times the work of the last one at N = 4096: the order is then
+// block-major, every head's heaviest block first.  Consecutive ids go to the
+// dies in turn, so id % n_heads = head keeps each head on one die when the
+// head count is a multiple of kNumXcd.  Other masks give every key block
+// about the same work and keep the head-major order of fwd_work_item, where
+// the blocks of a head run side by side and share its streamed Q/dO tiles in
+// L2.
+ATTN_HD void kv_work_item(int64_t wg, int64_t n_heads, int64_t n_kblk, int mode, int64_t* head,
+                          int64_t* kblk) {
+  if (mode == kCausal) {
+    *head = wg % n_heads;
+    *kblk = wg / n_heads;
+  } else {
+    fwd_work_item(wg, n_heads, n_kblk, kNone, head, kblk);
+  }
+}
+
 }  // namespace attn

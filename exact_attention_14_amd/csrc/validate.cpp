@@ -210,4 +210,15 @@ attn_status attn_fwd_workgroup(int64_t wg, int64_t n_heads, int64_t n_qblk, attn
   return ATTN_OK;
 }
 
+attn_status attn_bwd_kv_workgroup(int64_t wg, int64_t n_heads, int64_t n_kblk,
+                                  attn_mask_mode mode, int64_t* head, int64_t* kblk) {
+  if (head == nullptr || kblk == nullptr) return ATTN_E_NULLPTR;
+  if (n_heads < 1 || n_kblk < 1 || n_heads > attn::kMaxI32 || n_kblk > attn::kMaxI32 ||
+      n_heads * n_kblk > attn::kMaxI32 || wg < 0 || wg >= n_heads * n_kblk)
+    return ATTN_E_SHAPE;
+  if (attn::check_mask(mode, 0, 0) != ATTN_OK) return ATTN_E_MASK;
+  attn::kv_work_item(wg, n_heads, n_kblk, mode, head, kblk);
+  return ATTN_OK;
+}
+
 }  // extern "C"

@@ -183,6 +183,17 @@ attn_status attn_kv_tile_range(int64_t N, int64_t q0, int64_t block_q, int64_t b
 attn_status attn_fwd_workgroup(int64_t wg, int64_t n_heads, int64_t n_qblk, attn_mask_mode mode,
                                int64_t* head, int64_t* qblk);
 
+/*
+ * attn_bwd_kv_workgroup -- which (head index b*H + h, key block) workgroup
+ * `wg` of the backward's key-major dK/dV pass (n_wg = B*H*n_kblk) processes.
+ * With a causal mask the order is key-block-major, all heads' first (most
+ * loaded: it sees every query tile) key blocks first; otherwise it is the
+ * forward's head-major order.  Returns ATTN_E_SHAPE if wg is out of range,
+ * ATTN_E_MASK for an unknown mode, ATTN_E_NULLPTR for null outputs.
+ */
+attn_status attn_bwd_kv_workgroup(int64_t wg, int64_t n_heads, int64_t n_kblk,
+                                  attn_mask_mode mode, int64_t* head, int64_t* kblk);
+
 #ifdef __cplusplus
 }
 #endif

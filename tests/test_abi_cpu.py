@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     lib = ea.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -111,6 +111,39 @@ def test_workgroup_order_keeps_a_head_on_one_die():
         h, _ = ea.attn_fwd_workgroup(wg, n_heads, n_qblk, 0)
         die_heads.setdefault(h, set()).add(wg % 8)
     assert all(len(d) == 1 for d in die_heads.values())
+
+
+@pytest.mark.parametrize("n_heads,n_kblk", [(1, 1), (3, 5), (320, 16), (7, 3)])
+@pytest.mark.parametrize("mode", [0, 1, 2])
+def test_kv_workgroup_order_is_a_bijection(n_heads, n_kblk, mode):
+    seen = set()
+    n = n_heads * n_kblk
+    for wg in range(n):
+        h, kb = ea.attn_bwd_kv_workgroup(wg, n_heads, n_kblk, mode)
+        assert 0 <= h < n_heads and 0 <= kb < n_kblk
+        seen.add((h, kb))
+    assert len(seen) == n
+    with pytest.raises(ea.AttnError):
+        ea.attn_bwd_kv_workgroup(n, n_heads, n_kblk, mode)
+    with pytest.raises(ea.AttnError):
+        ea.attn_bwd_kv_workgroup(0, n_heads, n_kblk, 3)
+
+
+def test_causal_kv_order_is_heavy_first_and_keeps_heads_on_one_die():
+    """Causal: key block 0 (every query tile) of every head first, then block 1 ...;
+    ids are dealt round-robin to 8 dies, and with 320 heads each head stays on one."""
+    n_heads, n_kblk = 320, 16
+    die_heads, prev = {}, -1
+    for wg in range(n_heads * n_kblk):
+        h, kb = ea.attn_bwd_kv_workgroup(wg, n_heads, n_kblk, 1)
+        assert kb >= prev
+        prev = kb
+        die_heads.setdefault(h, set()).add(wg % 8)
+    assert all(len(d) == 1 for d in die_heads.values())
+    # other masks: the forward's head-major order
+    for wg in (0, 17, 5119):
+        assert ea.attn_bwd_kv_workgroup(wg, n_heads, n_kblk, 0) == ea.attn_fwd_workgroup(
+            wg, n_heads, n_kblk, 0)
 
 
 def test_causal_runs_longest_query_blocks_first():
