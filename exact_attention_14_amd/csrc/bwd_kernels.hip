@@ -7,7 +7,10 @@
 // is exp(scale * q.k - lse) directly -- no running max is needed.
 //
 // Three launches, no atomics, so the result is deterministic:
-//   1. bwd_rowdot:  D_i = dO_i . O_i from the forward's stored O (fp32).
+//   1. bwd_rowdot:  D_i = dO_i . O_i from the forward's stored O (fp32),
+//                   stored negated, and each row's score offset
+//                   lse_i * lse_mul, so that the later passes can start
+//                   their accumulators from them.
 //   2. bwd_dq:      query-major like the forward.  Per 64-key tile, 32 keys
 //                   at a time: S^T = K Q^T, P^T, dP^T = V dO^T,
 //                   dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.  Q and dO stay
@@ -57,7 +60,10 @@ __global__ __launch_bounds__(256) void bwd_rowdot_kernel(BwdParams p, int64_t ro
   }
 #pragma unroll
   for (int w = NCH / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w, NCH);
-  if (row < rows && ch == 0) p.Dsum[row] = acc;
+  if (row < rows && ch == 0) {
+    p.Dneg[row] = -acc;
+    p.Loff[row] = p.lse[row] * p.lse_mul;
+  }
 }
 
 // A 64-row tile of a [rows][D] 16-bit matrix in LDS: row-major, 16-byte
@@ -182,7 +188,7 @@ void bwd_dq_kernel(BwdParams p, int n_qblk) {
     gf[kk] = buf_load16(rG, off, 0);
   }
   const float lse2 = qrow < N ? p.lse[static_cast<size_t>(head) * N + qrow] * kLog2e : INFINITY;
-  const float Dq = qrow < N ? p.Dsum[static_cast<size_t>(head) * N + qrow] : 0.0f;
+  const float Dq = qrow < N ? p.Dneg[static_cast<size_t>(head) * N + qrow] : 0.0f;  // -D
   const float c = p.c;
 
   f32x16_t acc[DBLK];
@@ -227,7 +233,7 @@ void bwd_dq_kernel(BwdParams p, int n_qblk) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int i = 2 * j + u;
-          e[u] = fast_exp2(fmaf(s[i], c, -lse2)) * (dp[i] - Dq);
+          e[u] = fast_exp2(fmaf(s[i], c, -lse2)) * (dp[i] + Dq);
         }
         ds[j] = Elem<T>::pack2(e[0], e[1]);
       }
@@ -308,8 +314,8 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
   const auto rK = make_rsrc(reinterpret_cast<const char*>(p.K) + hoff, head_bytes);
   const auto rV = make_rsrc(reinterpret_cast<const char*>(p.V) + hoff, head_bytes);
   const auto rG = make_rsrc(reinterpret_cast<const char*>(p.dO) + hoff, head_bytes);
-  const auto rL = make_rsrc(p.lse + static_cast<size_t>(head) * N, static_cast<uint32_t>(N) * 4);
-  const auto rD = make_rsrc(p.Dsum + static_cast<size_t>(head) * N, static_cast<uint32_t>(N) * 4);
+  const auto rL = make_rsrc(p.Loff + static_cast<size_t>(head) * N, static_cast<uint32_t>(N) * 4);
+  const auto rD = make_rsrc(p.Dneg + static_cast<size_t>(head) * N, static_cast<uint32_t>(N) * 4);
 
   // K (with a negative scale's sign flip folded in) and V as B operands of
   // S = Q K^T and dP = dO V^T: lane (key r32 of block kb, half).
@@ -345,10 +351,9 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
   const TileLoader<D, NW> ld(wave, lane);
   const TileReaders<D> rd(lane);
 
-  // lse and D of a query tile, one 4-byte direct load each (wavefront 0;
-  // rows past N read as zero and are masked).  Once landed they are turned
-  // into the starting values of the score and dP accumulators:
-  // -lse * log2(e) / c and -D.
+  // The score offsets and -D of a query tile (the starting values of the
+  // score and dP accumulators), one 4-byte direct load each by wavefront 0;
+  // rows past N read as zero and are masked.
   auto load_stats = [&](int q0, float* sl, float* sd) {
     if (wave == 0) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rL, (__attribute__((address_space(3))) void*)(sl), 4,
@@ -451,19 +456,10 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
     }
   };
 
-  // The wavefront that loaded a tile's statistics converts them once its own
-  // direct loads have landed (the barrier that follows publishes them).
-  auto convert_stats = [&](float* sl, float* sd) {
-    if (wave == 0) {
-      sl[lane] *= p.lse_mul;
-      sd[lane] = -sd[lane];
-    }
-  };
   ld.load(rQ, q_lds0, lo * BQ);
   ld.load(rG, g_lds0, lo * BQ);
   load_stats(lo * BQ, s_lse0, s_d0);
   wait_vmem();
-  convert_stats(s_lse0, s_d0);
   __syncthreads();
   for (int t = lo; t < hi; t += 2) {
     if (t + 1 < hi) {
@@ -473,7 +469,6 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
     }
     tile(t, q_lds0, g_lds0, s_lse0, s_d0);
     wait_vmem();
-    convert_stats(s_lse1, s_d1);
     __syncthreads();
     if (t + 1 >= hi) break;
     if (t + 2 < hi) {
@@ -483,7 +478,6 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
     }
     tile(t + 1, q_lds1, g_lds1, s_lse1, s_d1);
     wait_vmem();
-    convert_stats(s_lse0, s_d0);
     __syncthreads();
   }
 

@@ -30,14 +30,15 @@ struct BwdParams {
   void* dQ;
   void* dK;
   void* dV;
-  float* Dsum;    // workspace: D_i = dO_i . O_i, [n_heads * N]
+  float* Dneg;    // workspace: -D_i = -(dO_i . O_i), [n_heads * N]
+  float* Loff;    // workspace: lse_i * lse_mul, a row's score offset, [n_heads * N]
   int N;
   int n_heads;
   int wl, wr;
   float c;        // |scale| * log2(e), at least 1e-30
   float scale;    // the signed scale (applied to dQ and dK)
   uint32_t qsign; // sign flip folded into Q for negative scales
-  float lse_mul;  // -log2(e) / c: lse * lse_mul is a row's offset in score units
+  float lse_mul;  // -log2(e) / c: exp2(c * (s + lse * lse_mul)) = exp(scale * q.k - lse)
 };
 
 hipError_t launch_fwd(const FwdParams& p, int dt_bf16, int d, int mode, int64_t n_wg,

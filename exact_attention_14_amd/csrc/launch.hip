@@ -62,7 +62,9 @@ attn_status attn_bwd(attn_dtype dt, const void* Q, const void* K, const void* V,
   attn::BwdParams p{};
   p.Q = Q; p.K = K; p.V = V; p.O = O; p.lse = lse; p.dO = dO;
   p.dQ = dQ; p.dK = dK; p.dV = dV;
-  p.Dsum = static_cast<float*>(workspace);
+  p.Dneg = static_cast<float*>(workspace);
+  p.Loff = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                    attn::row_array_bytes(B, H, N));
   p.N = static_cast<int>(N);
   p.n_heads = static_cast<int>(B * H);
   p.wl = mode == ATTN_MASK_SLIDING ? attn::clip_window(window_left, N) : 0;

@@ -85,9 +85,10 @@ attn_status check_common(const TensorArgs& a) {
   return ATTN_OK;
 }
 
+// Two float32 arrays of one value per row, each padded to 256 bytes: -D_i
+// and the row's score offset -lse_i * log2(e) / c (see BwdParams).
 uint64_t workspace_bytes(int64_t B, int64_t H, int64_t N) {
-  uint64_t rows = static_cast<uint64_t>(B) * H * N;
-  return (rows * 4u + 255u) / 256u * 256u;
+  return 2u * row_array_bytes(B, H, N);
 }
 
 attn_status fwd_check(int dt, const void* Q, const void* K, const void* V, const void* O,

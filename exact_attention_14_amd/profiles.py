@@ -2,7 +2,7 @@
 
     python -m exact_attention_14_amd.profiles stats  <kernel_stats.csv> <out.md> <command...>
     python -m exact_attention_14_amd.profiles traffic <fetch_dir> <write_dir> <workload> <copy_mib> <out.json> <out.md>
-    python -m exact_attention_14_amd.profiles counters <counter_dir> <kernel_stats.csv> <out.md> <command...>
+    python -m exact_attention_14_amd.profiles counters [--clock-ghz=F] <counter_dir> <kernel_stats.csv> <out.md> <command...>
 
 ``stats`` turns the ``*_kernel_stats.csv`` of ``rocprofv3 --kernel-trace --stats
 --output-format csv`` into a short markdown table.  ``traffic`` reads two
@@ -13,9 +13,8 @@ counters by what the same counters read for the calibration copy of M MiB
 per launch.  The JSON records a hash of the forward kernel's sources so that
 bench.py reports the traffic only while the kernel is unchanged.  ``counters``
 summarises one ``--pmc`` pass (per-dispatch means of every attention kernel
-in it) and derives each kernel's clock and matrix-core busy fraction:
-GRBM_GUI_ACTIVE is summed over the 8 dies and SQ_VALU_MFMA_BUSY_CYCLES over
-the 1024 SIMDs.
+in it): matrix-core busy cycles per SIMD and, given the shader clock read
+with amd-smi under the same load, the busy fraction.
 """
 from __future__ import annotations
 
@@ -105,7 +104,8 @@ def traffic(fetch_dir: str, write_dir: str, workload: str, copy_mib: int, out_js
         f.write("\n".join(lines))
 
 
-def counters(counter_dir: str, kernel_stats: str, out_md: str, command: str) -> None:
+def counters(counter_dir: str, kernel_stats: str, out_md: str, command: str,
+             clock_ghz: float = 0.0) -> None:
     keys = ("fwd_kernel", "bwd_rowdot_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel")
     per = {}  # kernel -> counter -> dispatch -> value
     for path in glob.glob(os.path.join(counter_dir, "*counter_collection.csv")):
@@ -122,8 +122,10 @@ def counters(counter_dir: str, kernel_stats: str, out_md: str, command: str) -> 
             durations[key] = float(r["AverageNs"])
     lines = ["# Kernel counters (rocprofv3 PMC)", "", f"Command: `{command}`", "",
              "Means per dispatch; durations are the averages from the kernel trace of the same",
-             "workload.  GRBM_GUI_ACTIVE is summed over the 8 dies, SQ_VALU_MFMA_BUSY_CYCLES over",
-             "the 1024 SIMDs.", ""]
+             "workload.  SQ_VALU_MFMA_BUSY_CYCLES is summed over the 1024 SIMDs.  GRBM_GUI_ACTIVE",
+             "does not count shader-clock cycles (divided by the duration it gives neither the",
+             "clock amd-smi reports nor a constant multiple of it), so no clock is derived from it.",
+             ""]
     for key in keys:
         if key not in per:
             continue
@@ -133,14 +135,15 @@ def counters(counter_dir: str, kernel_stats: str, out_md: str, command: str) -> 
             lines += [f"Kernel duration: {durations[key] / 1e3:.1f} us", ""]
         lines += ["| counter | mean per dispatch |", "|---|---|"]
         lines += [f"| {k} | {v:.4g} |" for k, v in sorted(mean.items())]
-        if "GRBM_GUI_ACTIVE" in mean and key in durations:
-            cycles = mean["GRBM_GUI_ACTIVE"] / 8
-            lines += ["", f"- cycles per die: {cycles:.4g}; clock = cycles / duration = "
-                          f"{cycles / durations[key]:.2f} GHz"]
-            if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
-                lines.append(f"- matrix cores busy: "
-                             f"{mean['SQ_VALU_MFMA_BUSY_CYCLES'] / 1024 / cycles:.1%} of cycles "
-                             "(per SIMD)")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and key in durations:
+            busy = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024
+            lines += ["", f"- matrix-core busy cycles per SIMD: {busy:.4g}"]
+            if "SQ_INSTS_MFMA" in mean:
+                lines.append(f"- matrix instructions per SIMD: {mean['SQ_INSTS_MFMA'] / 1024:.4g} "
+                             f"({busy / (mean['SQ_INSTS_MFMA'] / 1024):.1f} busy cycles each)")
+            if clock_ghz:
+                lines.append(f"- busy fraction at the {clock_ghz:.2f} GHz shader clock amd-smi "
+                             f"reports under this load: {busy / (durations[key] * clock_ghz):.1%}")
         lines.append("")
     with open(out_md, "w") as f:
         f.write("\n".join(lines))
@@ -150,7 +153,12 @@ if __name__ == "__main__":
     if sys.argv[1] == "stats":
         stats(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
     elif sys.argv[1] == "counters":
-        counters(sys.argv[2], sys.argv[3], sys.argv[4], " ".join(sys.argv[5:]))
+        args = sys.argv[2:]
+        clk = 0.0
+        if args and args[0].startswith("--clock-ghz="):
+            clk = float(args[0].split("=", 1)[1])
+            args = args[1:]
+        counters(args[0], args[1], args[2], " ".join(args[3:]), clk)
     elif sys.argv[1] == "traffic":
         traffic(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5]), sys.argv[6], sys.argv[7])
     else:

@@ -103,7 +103,9 @@ attn_status attn_fwd(attn_dtype dt, const void* Q, const void* K, const void* V,
 
 /*
  * attn_bwd_workspace_bytes -- size in bytes of the device workspace attn_bwd
- * needs for these sizes (float32 D_i = dO_i . O_i per row, padded to 256 B).
+ * needs for these sizes: two float32 values per row (-D_i with
+ * D_i = dO_i . O_i, and the row's lse rescaled to the score units the
+ * kernels use), each array padded to 256 B.
  * Returns 0 if the sizes are invalid.  Pure host function, no HIP call.
  */
 size_t attn_bwd_workspace_bytes(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d);
