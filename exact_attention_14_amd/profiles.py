@@ -135,10 +135,10 @@ def counters(counter_dir: str, kernel_stats: str, out_md: str, command: str,
             lines += [f"Kernel duration: {durations[key] / 1e3:.1f} us", ""]
         lines += ["| counter | mean per dispatch |", "|---|---|"]
         lines += [f"| {k} | {v:.4g} |" for k, v in sorted(mean.items())]
-        if "SQ_VALU_MFMA_BUSY_CYCLES" in mean and key in durations:
+        if mean.get("SQ_VALU_MFMA_BUSY_CYCLES", 0) > 0 and key in durations:
             busy = mean["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024
             lines += ["", f"- matrix-core busy cycles per SIMD: {busy:.4g}"]
-            if "SQ_INSTS_MFMA" in mean:
+            if mean.get("SQ_INSTS_MFMA", 0) > 0:
                 lines.append(f"- matrix instructions per SIMD: {mean['SQ_INSTS_MFMA'] / 1024:.4g} "
                              f"({busy / (mean['SQ_INSTS_MFMA'] / 1024):.1f} busy cycles each)")
             if clock_ghz:
