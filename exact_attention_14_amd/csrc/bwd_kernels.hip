@@ -16,9 +16,8 @@
 //                   dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.  Q and dO stay
 //                   in registers; two wavefronts per SIMD.
 //   3. bwd_dkdv:    key-major.  Per 64-query tile, 32 queries at a time:
-//                   S = Q K^T, P, dP = dO V^T, dS = P (dP - D) (the
-//                   offsets lse and D enter as the accumulators' starting
-//                   values),
+//                   S = Q K^T, P, dP = dO V^T, dS = P (dP - D) (the rows'
+//                   offsets and -D are the accumulators' starting values),
 //                   dV^T += dO^T P, dK^T += Q^T dS.  K and V stay in
 //                   registers; each wavefront owns 64 keys (two blocks that
 //                   share every operand read from LDS) with its dV and dK
@@ -299,7 +298,7 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
   constexpr uint32_t ROWB = L::ROWB;
   __shared__ __attribute__((aligned(16))) char q_lds0[L::BYTES], q_lds1[L::BYTES];
   __shared__ __attribute__((aligned(16))) char g_lds0[L::BYTES], g_lds1[L::BYTES];
-  __shared__ __attribute__((aligned(16))) float s_lse0[BQ], s_lse1[BQ], s_d0[BQ], s_d1[BQ];
+  __shared__ __attribute__((aligned(16))) float s_off0[BQ], s_off1[BQ], s_dn0[BQ], s_dn1[BQ];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, half = lane >> 5, r32 = lane & 31;
@@ -458,25 +457,25 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
 
   ld.load(rQ, q_lds0, lo * BQ);
   ld.load(rG, g_lds0, lo * BQ);
-  load_stats(lo * BQ, s_lse0, s_d0);
+  load_stats(lo * BQ, s_off0, s_dn0);
   wait_vmem();
   __syncthreads();
   for (int t = lo; t < hi; t += 2) {
     if (t + 1 < hi) {
       ld.load(rQ, q_lds1, (t + 1) * BQ);
       ld.load(rG, g_lds1, (t + 1) * BQ);
-      load_stats((t + 1) * BQ, s_lse1, s_d1);
+      load_stats((t + 1) * BQ, s_off1, s_dn1);
     }
-    tile(t, q_lds0, g_lds0, s_lse0, s_d0);
+    tile(t, q_lds0, g_lds0, s_off0, s_dn0);
     wait_vmem();
     __syncthreads();
     if (t + 1 >= hi) break;
     if (t + 2 < hi) {
       ld.load(rQ, q_lds0, (t + 2) * BQ);
       ld.load(rG, g_lds0, (t + 2) * BQ);
-      load_stats((t + 2) * BQ, s_lse0, s_d0);
+      load_stats((t + 2) * BQ, s_off0, s_dn0);
     }
-    tile(t + 1, q_lds1, g_lds1, s_lse1, s_d1);
+    tile(t + 1, q_lds1, g_lds1, s_off1, s_dn1);
     wait_vmem();
     __syncthreads();
   }
