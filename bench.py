@@ -124,19 +124,26 @@ def main():
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
 
-    ms_wall = (t1 - t0) * 1e3 / args.steps
-    ms_kernel = ev0.elapsed_time(ev1) / args.steps
+    def timed(fn):
+        """Wall time of args.steps calls (host clock, synchronised on both sides)
+        and the calls' GPU times from events recorded between them on the
+        launch stream: (wall ms per call, mean GPU ms per call, percentiles)."""
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        torch.cuda.synchronize()
+        ta = time.perf_counter()
+        evs[0].record(stream)
+        for i in range(args.steps):
+            fn()
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        tb = time.perf_counter()
+        per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+        pct = {f"p{q}": round(per[min(len(per) - 1, (len(per) * q) // 100)], 5)
+               for q in (10, 50, 90)}
+        return (tb - ta) * 1e3 / args.steps, evs[0].elapsed_time(evs[-1]) / args.steps, pct
+
+    ms_wall, ms_kernel, per_call = timed(step)
     flops = fwd_flops(w)
     value = flops / (ms_wall * 1e-3) / 1e12
     achieved = flops / (ms_kernel * 1e-3) / 1e12
@@ -155,18 +162,11 @@ def main():
 
         for _ in range(args.warmup):
             bstep()
-        torch.cuda.synchronize()
-        tb0 = time.perf_counter()
-        ev0.record(stream)
-        for _ in range(args.steps):
-            bstep()
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        tb1 = time.perf_counter()
-        b_ms = ev0.elapsed_time(ev1) / args.steps
+        b_wall, b_ms, b_pct = timed(bstep)
         bflops = 10 * w.d * w.B * w.H * allowed_pairs(w.N, w.mask, w.window_left, w.window_right)
-        backward = {"ms_per_call": round((tb1 - tb0) * 1e3 / args.steps, 5),
+        backward = {"ms_per_call": round(b_wall, 5),
                     "kernel_ms": round(b_ms, 5),
+                    "kernel_ms_per_call": b_pct,
                     "tflops": round(bflops / (b_ms * 1e-3) / 1e12, 3),
                     "frac_of_peak": round(bflops / (b_ms * 1e-3) / 1e12 / PEAK_TFLOPS[w.dtype], 4),
                     "flop_per_call": bflops,
@@ -214,6 +214,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": traffic,
                      "kernel": "fwd_kernel", "kernel_ms": round(ms_kernel, 5),
+                     "kernel_ms_per_call": per_call,
                      "flop_per_launch": flops},
     }
     if backward is not None:
