@@ -116,6 +116,18 @@ def _stream_ptr(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _check_gpu(q: torch.Tensor):
+    if not q.is_cuda:
+        raise ValueError("inputs must be on a GPU")
+
+
+def _check_lse(lse: torch.Tensor, q: torch.Tensor):
+    B, H, N, _ = q.shape
+    if (tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous()
+            or lse.device != q.device):
+        raise ValueError(f"lse must be contiguous float32 [B, H, N] on {q.device}")
+
+
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, mask=None, scale=None,
              out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
     """Forward pass; returns (O, lse).  Inputs: contiguous [B, H, N, d] on a GPU.
@@ -128,8 +140,7 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, mask=None, sc
     _check4("k", k, q)
     _check4("v", v, q)
     _check4("q", q, q)
-    if not q.is_cuda:
-        raise ValueError("inputs must be on a GPU")
+    _check_gpu(q)
     B, H, N, d = q.shape
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -141,11 +152,13 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, mask=None, sc
         _check4("out", out, q)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    elif lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 [B, H, N]")
-    st = lib().attn_fwd(dt, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                        lse.data_ptr(), B, H, N, d, float(scale), mode, wl, wr,
-                        _stream_ptr(q.device))
+    else:
+        _check_lse(lse, q)
+    # The library launches on the calling thread's current device.
+    with torch.cuda.device(q.device):
+        st = lib().attn_fwd(dt, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                            lse.data_ptr(), B, H, N, d, float(scale), mode, wl, wr,
+                            _stream_ptr(q.device))
     _raise("attn_fwd", st)
     return out, lse
 
@@ -157,12 +170,14 @@ def attn_bwd_workspace_bytes(dtype: torch.dtype, B: int, H: int, N: int, d: int)
 
 def attn_bwd(q, k, v, o, lse, do, *, mask=None, scale=None, workspace=None):
     """Recomputation backward; returns (dQ, dK, dV) for upstream gradient ``do``."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
     _check4("q", q, q)
     for name, t in (("k", k), ("v", v), ("o", o), ("do", do)):
         _check4(name, t, q)
+    _check_gpu(q)
+    _check_lse(lse, q)
     B, H, N, d = q.shape
-    if lse.shape != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 [B, H, N]")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     mode, wl, wr = mask_args(mask)
@@ -170,11 +185,15 @@ def attn_bwd(q, k, v, o, lse, do, *, mask=None, scale=None, workspace=None):
     need = attn_bwd_workspace_bytes(q.dtype, B, H, N, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    elif workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {q.device}")
+    ws_bytes = workspace.numel() * workspace.element_size()
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    st = lib().attn_bwd(dt, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                        lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                        dv.data_ptr(), workspace.data_ptr(), workspace.numel(), B, H, N, d,
-                        float(scale), mode, wl, wr, _stream_ptr(q.device))
+    with torch.cuda.device(q.device):
+        st = lib().attn_bwd(dt, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                            lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                            dv.data_ptr(), workspace.data_ptr(), ws_bytes, B, H, N, d,
+                            float(scale), mode, wl, wr, _stream_ptr(q.device))
     _raise("attn_bwd", st)
     return dq, dk, dv
 

@@ -151,3 +151,16 @@ def test_causal_runs_longest_query_blocks_first():
     assert qb0 == 15
     h0, qb0 = ea.attn_fwd_workgroup(0, 4, 16, 0)
     assert qb0 == 0
+
+
+def test_binding_rejects_host_tensors_before_any_library_call():
+    """CPU tensors never reach the kernels: the binding raises first."""
+    import torch
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU"):
+        ea.attn_fwd(q, q, q)
+    lse = torch.zeros(1, 1, 8, dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU"):
+        ea.attn_bwd(q, q, q, q, lse, q)
+    with pytest.raises(ValueError, match="shape"):
+        ea.attn_bwd(q, q[:, :, :4], q, q, lse, q)

@@ -145,3 +145,23 @@ def test_output_buffers_and_errors():
         ea.attn_fwd(q, k, v, mask=(-1, 0))   # negative window
     with pytest.raises(ea.AttnError):
         ea.attn_fwd(q, k, v, scale=math.inf)
+
+
+def test_binding_checks_lse_and_workspace():
+    inp = draw(1, 2, 100, 64, "f16", 17, with_do=True)
+    q, k, v, do = (gpu(inp[x]) for x in ("q", "k", "v", "do"))
+    with pytest.raises(ValueError, match="lse"):
+        ea.attn_fwd(q, k, v, lse=torch.empty(1, 2, 100))          # host lse
+    o, lse = ea.attn_fwd(q, k, v)
+    with pytest.raises(ValueError, match="lse"):
+        ea.attn_bwd(q, k, v, o, lse.cpu(), do)
+    with pytest.raises(ValueError, match="workspace"):
+        ea.attn_bwd(q, k, v, o, lse, do, workspace=torch.empty(4096, dtype=torch.uint8))
+    # A workspace of any element type counts in bytes: float32 with exactly enough bytes works
+    # and matches the default workspace bitwise.
+    need = ea.attn_bwd_workspace_bytes(q.dtype, 1, 2, 100, 64)
+    ws = torch.empty((need + 3) // 4, dtype=torch.float32, device=q.device)
+    g1 = ea.attn_bwd(q, k, v, o, lse, do, workspace=ws)
+    g2 = ea.attn_bwd(q, k, v, o, lse, do)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(g1, g2))
