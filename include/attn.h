@@ -42,7 +42,10 @@
  *    allocates, frees or retains device memory and keeps no state between
  *    calls; it is thread-safe.  Inputs are read only.  Outputs must not overlap
  *    any input or each other (ATTN_E_ALIAS, checked by address range).
- *  - Device pointers must be 16-byte aligned (ATTN_E_ALIGN).
+ *  - Device pointers must be 16-byte aligned (ATTN_E_ALIGN).  All device
+ *    buffers and `stream` must belong to the calling thread's current HIP
+ *    device, on which the kernels are launched (the library cannot tell a
+ *    host pointer or another device's pointer from a valid one).
  *  - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL is the
  *    default stream) and the call returns without synchronising.
  *  - Errors: every argument is validated on the host before any HIP call; on
