@@ -47,8 +47,11 @@ attn_status check_sizes(int dt, int64_t B, int64_t H, int64_t N, int64_t d) {
   if (N * d * 2 > kMaxI32) return ATTN_E_SHAPE;
   const int64_t BH = B * H;
   if (BH > (int64_t(1) << 62) / (N * d * 4)) return ATTN_E_SHAPE;
-  // Grids: one workgroup per (head, 64-row block) at most.
+  // Grids: one workgroup per (head, 64-row block) at most, and at most 2^32
+  // threads per launch; the widest launch (the backward's row dots) uses d/8
+  // threads per row.
   if (BH * ceil_div(N, 64) > kMaxI32) return ATTN_E_SHAPE;
+  if (BH * N > (int64_t(1) << 32) / (d / 8) - 256) return ATTN_E_SHAPE;
   return ATTN_OK;
 }
 

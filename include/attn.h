@@ -36,7 +36,8 @@
  *  - Supported: dt in {F16, BF16}; d in {64, 128} (P3 §4: the head sizes the
  *    tiling is built for); N >= 1 with one head's rows below 2^31 bytes
  *    (N * d * 2 < 2^31, i.e. N < 8,388,608 at d = 128); B, H >= 1 with
- *    B * H < 2^31; any finite scale (negative and zero allowed).  Any N is
+ *    B * H < 2^31 and B * H * N * d / 8 below 2^32 - 2^11 (every launch stays
+ *    under 2^32 threads); any finite scale (negative and zero allowed).  Any N is
  *    handled (ragged tails are masked in-kernel, P2 "pitfall 1"), not padded.
  *  - Ownership: the caller allocates and owns every buffer.  The library never
  *    allocates, frees or retains device memory and keeps no state between

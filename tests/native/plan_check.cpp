@@ -149,6 +149,10 @@ int main() {
   CHECK(attn_fwd_check(ATTN_BF16, Q, K, V, O, L, INT64_MAX / 2, INT64_MAX / 2, N, d, 0.1f, ATTN_MASK_NONE, 0, 0) == ATTN_E_SHAPE, "BH");
   CHECK(attn_fwd_check(ATTN_BF16, Q, K, V, O, L, B, H, 8388608, 128, 0.1f, ATTN_MASK_NONE, 0, 0) == ATTN_E_SHAPE, "head bytes");
   CHECK(attn_fwd_check(ATTN_BF16, Q, K, V, O, L, B, H, 8388607, 128, 0.1f, ATTN_MASK_NONE, 0, 0) == ATTN_E_ALIAS, "head bytes ok (then aliasing of the tiny test buffers)");
+  // Launch width: B*H*N*d/8 threads (the backward's row dots) must stay below 2^32.
+  CHECK(attn_fwd_check(ATTN_BF16, Q, K, V, O, L, 64, 1, 4194304, 128, 0.1f, ATTN_MASK_NONE, 0, 0) == ATTN_E_SHAPE, "threads d128");
+  CHECK(attn_fwd_check(ATTN_BF16, Q, K, V, O, L, 63, 1, 4194304, 128, 0.1f, ATTN_MASK_NONE, 0, 0) == ATTN_E_ALIAS, "threads d128 ok");
+  CHECK(attn_fwd_check(ATTN_BF16, Q, K, V, O, L, 64, 1, 8388607, 64, 0.1f, ATTN_MASK_NONE, 0, 0) == ATTN_E_SHAPE, "threads d64");
   CHECK(attn_fwd_check(ATTN_BF16, Q, K, V, O, L, B, H, N, d, 0.1f, ATTN_MASK_SLIDING, -1, 0) == ATTN_E_MASK, "wl");
   CHECK(attn_fwd_check(ATTN_BF16, Q, K, V, O, L, B, H, N, d, 0.1f, (attn_mask_mode)9, 0, 0) == ATTN_E_MASK, "mode");
   CHECK(attn_fwd_check(ATTN_BF16, Q, K, V, O, L, B, H, N, d, 0.1f, ATTN_MASK_CAUSAL, -5, -5) == ATTN_OK, "windows ignored");
