@@ -184,26 +184,6 @@ __device__ __forceinline__ void wait_vmem_but() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-// Scheduling-group masks for __builtin_amdgcn_sched_group_barrier.
-constexpr int kSchedValu = 0x002;
-constexpr int kSchedMfma = 0x008;
-constexpr int kSchedDsRead = 0x100;
-
-// Asks the scheduler for a software-pipelined order: PRE groups of `reads`
-// LDS reads up front, then N times {one matrix instruction, `valu` vector-ALU
-// instructions, `reads` LDS reads for a later matrix instruction}, so that
-// LDS latency and independent vector work both hide behind the matrix core.
-template <int N, int READS, int VALU, int PRE>
-__device__ __forceinline__ void interleave_mfma() {
-  if (PRE * READS > 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PRE * READS, 0);
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-    if (VALU > 0) __builtin_amdgcn_sched_group_barrier(kSchedValu, VALU, 0);
-    if (READS > 0 && i + PRE < N) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, READS, 0);
-  }
-}
-
 // Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
 // lanes 4t .. 4t+3 point at the four 4-element pieces of row t of a 4 x 16
 // block of 16-bit elements; lane j of the group receives column j, i.e. the

@@ -233,60 +233,107 @@ void fwd_kernel(FwdParams p) {
     lr *= corr;
   };
 
-  // Phase 2: probabilities, rounded to 16 bits in B-operand order, and their
-  // fp32 row sum.
-  // Probabilities of a tile in the exp2 domain, rounded to 16 bits in
+  // Phase 2: probabilities in the exp2 domain, rounded to 16 bits in
   // B-operand order, and the lane's sum of them.  For bf16 the sum is over
   // the fp32 values (bf16 rounding, up to 2^-8 relative, is too coarse for
   // lse); for fp16 it is over the rounded values (at most 2^-11 relative,
   // well inside lse's tolerance), so that one sum serves as both l and l~.
+  // prob_pair handles pair pi (0..15: block pi / 8, elements 2j, 2j + 1).
+  auto prob_pair = [&](f32x16_t s[2], float base, uint32_t pk[2][8], float rsum[2], int pi) {
+    const int kb = pi / 8, j = pi % 8;
+    const float e0 = fast_exp2(fmaf(s[kb][2 * j], c, -base));
+    const float e1 = fast_exp2(fmaf(s[kb][2 * j + 1], c, -base));
+    pk[kb][j] = Elem<T>::pack2(e0, e1);
+    if (kOneSum)
+      rsum[kb] = Elem<T>::add_pair(pk[kb][j], rsum[kb]);
+    else
+      rsum[kb] += e0 + e1;
+  };
   auto softmax_exp = [&](f32x16_t s[2], float base, uint32_t pk[2][8]) -> float {
-    float rs[2] = {0.0f, 0.0f};
+    float rsum[2] = {0.0f, 0.0f};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float e0 = fast_exp2(fmaf(s[kb][2 * j], c, -base));
-        const float e1 = fast_exp2(fmaf(s[kb][2 * j + 1], c, -base));
-        pk[kb][j] = Elem<T>::pack2(e0, e1);
-        if (kOneSum)
-          rs[kb] = Elem<T>::add_pair(pk[kb][j], rs[kb]);
-        else
-          rs[kb] += e0 + e1;
-      }
-    return rs[0] + rs[1];
+    for (int pi = 0; pi < 16; ++pi) prob_pair(s, base, pk, rsum, pi);
+    return rsum[0] + rsum[1];
   };
 
-  // Phase 3: O^T += V^T P^T over four 16-key steps (DBLK independent chains)
-  // and the row sum of the rounded probabilities.
+  // Phases 1 and 2 of a pipeline step as one explicitly ordered stream: the
+  // scores of the next tile (two chains, one per 32-key block) with the
+  // probabilities of the current tile, one pair after each matrix
+  // instruction.  K operands are read two reduction steps ahead from a
+  // three-deep ring; the scheduling barrier after each step keeps the
+  // compiler from regrouping (left to itself it read each operand one
+  // instruction ahead and waited on most reads).
+  auto scores_softmax = [&](const char* kb_, f32x16_t nxt[2], f32x16_t cur[2], float base,
+                            uint32_t pk[2][8]) -> float {
+    constexpr int PAIRS_PER_MMA = (16 + 2 * KSTEPS - 1) / (2 * KSTEPS);
+    float rsum[2] = {0.0f, 0.0f};
+    nxt[0] = f32x16_t{};
+    nxt[1] = f32x16_t{};
+    u32x4_t kop[3][2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+        kop[kk][kb] = ld_lds16(kb_ + kr_off + kb * 32 * L::K_PITCH + kk * 32);
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      if (kk + 2 < KSTEPS) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          kop[(kk + 2) % 3][kb] = ld_lds16(kb_ + kr_off + kb * 32 * L::K_PITCH + (kk + 2) * 32);
+      }
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        nxt[kb] = Elem<T>::mma(kop[kk % 3][kb], qf[kk], nxt[kb]);
+#pragma unroll
+        for (int r = 0; r < PAIRS_PER_MMA; ++r) {
+          const int pi = 2 * kk + kb + r * 2 * KSTEPS;
+          if (pi < 16) prob_pair(cur, base, pk, rsum, pi);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return rsum[0] + rsum[1];
+  };
+
+  // Phase 3: O^T += V^T P^T over four 16-key steps, the DBLK chains
+  // interleaved, with V^T operands read one step ahead (double-buffered), and
+  // the row sum of the rounded probabilities.
   auto pv_sums = [&](const char* vb_, uint32_t pk[2][8]) {
+    auto vread = [&](int ks, int db) {
+      const char* va = vb_ + vr_off[db] + ks * 16 * L::V_PITCH;
+      const u32x2_t lo2 = ld_lds_tr8(va);
+      const u32x2_t hi2 = ld_lds_tr8(va + 8 * L::V_PITCH);
+      return u32x4_t{lo2[0], lo2[1], hi2[0], hi2[1]};
+    };
+    u32x4_t vop[2][DBLK];
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) vop[0][db] = vread(0, db);
+    float rr = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < BC / 16; ++ks) {
+      if (ks + 1 < BC / 16) {
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) vop[(ks + 1) % 2][db] = vread(ks + 1, db);
+      }
       const u32x4_t b = {pk[ks >> 1][(ks & 1) * 4 + 0], pk[ks >> 1][(ks & 1) * 4 + 1],
                          pk[ks >> 1][(ks & 1) * 4 + 2], pk[ks >> 1][(ks & 1) * 4 + 3]};
 #pragma unroll
-      for (int db = 0; db < DBLK; ++db) {
-        const char* va = vb_ + vr_off[db] + ks * 16 * L::V_PITCH;
-        const u32x2_t lo2 = ld_lds_tr8(va);
-        const u32x2_t hi2 = ld_lds_tr8(va + 8 * L::V_PITCH);
-        const u32x4_t a = {lo2[0], lo2[1], hi2[0], hi2[1]};
-        acc[db] = Elem<T>::mma(a, b, acc[db]);
+      for (int db = 0; db < DBLK; ++db) acc[db] = Elem<T>::mma(vop[ks % 2][db], b, acc[db]);
+      if (!kOneSum) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) rr = Elem<T>::add_pair(b[u], rr);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (!kOneSum) {
-      float rr[2] = {0.0f, 0.0f};
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) rr[kb] = Elem<T>::add_pair(pk[kb][j], rr[kb]);
-      lr += rr[0] + rr[1];
-    }
+    if (!kOneSum) lr += rr;
   };
 
   // Software pipeline.  Iteration t computes the scores of tile t+1 (K stage
-  // (t+1-lo)%2) while it runs the softmax and the output product of tile t
-  // (V stage (t-lo)%2), so the matrix cores and the vector ALUs have
-  // independent work in the same instruction stream.  Meanwhile K of tile t+2
+  // (t+1-lo)%2) interleaved with the softmax of tile t, then the output
+  // product of tile t (V stage (t-lo)%2), so the matrix cores and the vector
+  // ALUs have independent work in the same instruction stream (the order is
+  // fixed in scores_softmax and pv_sums).  Meanwhile K of tile t+2
   // and V of tile t+1 travel from HBM straight into the LDS stages freed one
   // iteration ago.  The scores of the (nonexistent) tile after the last are
   // computed from whatever the stage holds and never used.
@@ -309,9 +356,7 @@ void fwd_kernel(FwdParams p) {
     if (has1) gload_v_lds(t + 1, P ? v_lds0 : v_lds1);
     apply_mask(t, cur);
     uint32_t pk[2][8];
-    scores(P ? k_lds0 : k_lds1, nxt);
-    float rs = softmax_exp(cur, m == -INFINITY ? 0.0f : m, pk);
-    interleave_mfma<2 * KSTEPS, 1, 6, 2>();
+    float rs = scores_softmax(P ? k_lds0 : k_lds1, nxt, cur, m == -INFINITY ? 0.0f : m, pk);
     // Optimistic softmax: the probabilities used the running max; if one of
     // them exceeds 2^kTau (their sum does) or the row has no max yet, take
     // the exact tile max, rescale and recompute (rare).
@@ -321,7 +366,6 @@ void fwd_kernel(FwdParams p) {
     }
     l += rs;
     pv_sums(P ? v_lds1 : v_lds0, pk);
-    interleave_mfma<DBLK * BC / 16, 2, 1, 2>();
     wait_vmem();
     __syncthreads();
   };
