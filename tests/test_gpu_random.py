@@ -5,6 +5,8 @@ The hand-written cases elsewhere pin the edges one by one; this sweep draws
 combinations nobody listed (odd lengths with odd windows, negative scales with
 sliding masks, ...) from a fixed seed, so a failure reproduces by its id.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -49,8 +51,10 @@ def cfg_id(c):
     return f"B{B}H{H}N{N}d{d}-{dtype}-{mask}-s{scale}".replace(" ", "")
 
 
-FWD = draw_configs(48, 7)
-BWD = draw_configs(24, 8, min_n=16, min_window=1)
+# ATTN_SWEEP_SCALE multiplies the number of cases (default 1: 48 forward, 24 backward).
+SCALE = max(1, int(os.environ.get("ATTN_SWEEP_SCALE", "1")))
+FWD = draw_configs(48 * SCALE, 7)
+BWD = draw_configs(24 * SCALE, 8, min_n=16, min_window=1)
 
 
 @pytest.mark.parametrize("cfg", FWD, ids=[cfg_id(c) for c in FWD])
