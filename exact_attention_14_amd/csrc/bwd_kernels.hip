@@ -6,16 +6,15 @@
 // and relies on recomputation).  With lse saved by the forward, a tile of P
 // is exp(scale * q.k - lse) directly -- no running max is needed.
 //
-// Three launches, no atomics, so the result is deterministic:
-//   1. bwd_rowdot:  D_i = dO_i . O_i from the forward's stored O (fp32),
-//                   stored negated, and each row's score offset
-//                   lse_i * lse_mul, so that the later passes can start
-//                   their accumulators from them.
-//   2. bwd_dq:      query-major like the forward.  Per 64-key tile, 32 keys
+// Two launches, no atomics, so the result is deterministic:
+//   1. bwd_dq:      query-major like the forward.  D_i = dO_i . O_i from the
+//                   forward's stored O (fp32), written negated for the
+//                   second pass together with each row's score offset
+//                   lse_i * lse_mul.  Per 64-key tile, 32 keys
 //                   at a time: S^T = K Q^T, P^T, dP^T = V dO^T,
 //                   dS^T = P^T (dP^T - D), dQ^T += K^T dS^T.  Q and dO stay
 //                   in registers; two wavefronts per SIMD.
-//   3. bwd_dkdv:    key-major.  Per 64-query tile, 32 queries at a time:
+//   2. bwd_dkdv:    key-major.  Per 64-query tile, 32 queries at a time:
 //                   S = Q K^T, P, dP = dO V^T, dS = P (dP - D) (the rows'
 //                   offsets and -D are the accumulators' starting values),
 //                   dV^T += dO^T P, dK^T += Q^T dS.  K and V stay in
@@ -39,31 +38,6 @@
 
 namespace attn {
 namespace {
-
-// ------------------------------------------------------------------ D_i
-template <typename T, int D>
-__global__ __launch_bounds__(256) void bwd_rowdot_kernel(BwdParams p, int64_t rows) {
-  constexpr int NCH = D / 8;
-  constexpr int ROWS_PER_WG = 256 / NCH;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * ROWS_PER_WG + threadIdx.x / NCH;
-  const int ch = threadIdx.x % NCH;
-  float acc = 0.0f;
-  if (row < rows) {
-    const size_t off = (static_cast<size_t>(row) * D + ch * 8) * 2;
-    const u32x4_t o = ld_global16(reinterpret_cast<const char*>(p.O) + off);
-    const u32x4_t g = ld_global16(reinterpret_cast<const char*>(p.dO) + off);
-    const T* ov = reinterpret_cast<const T*>(&o);
-    const T* gv = reinterpret_cast<const T*>(&g);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc = fmaf(static_cast<float>(ov[e]), static_cast<float>(gv[e]), acc);
-  }
-#pragma unroll
-  for (int w = NCH / 2; w >= 1; w >>= 1) acc += __shfl_xor(acc, w, NCH);
-  if (row < rows && ch == 0) {
-    p.Dneg[row] = -acc;
-    p.Loff[row] = p.lse[row] * p.lse_mul;
-  }
-}
 
 // A 64-row tile of a [rows][D] 16-bit matrix in LDS: row-major, 16-byte
 // chunk c of row r stored at chunk position c ^ swz(r).
@@ -176,18 +150,38 @@ void bwd_dq_kernel(BwdParams p, int n_qblk) {
   const auto rK = make_rsrc(reinterpret_cast<const char*>(p.K) + hoff, head_bytes);
   const auto rV = make_rsrc(reinterpret_cast<const char*>(p.V) + hoff, head_bytes);
   const auto rG = make_rsrc(reinterpret_cast<const char*>(p.dO) + hoff, head_bytes);
+  const auto rO = make_rsrc(reinterpret_cast<const char*>(p.O) + hoff, head_bytes);
 
+  // Q and dO of this lane's row stay in registers (B operands); the lane
+  // holds elements kk*16 + half*8 .. +7 of the row for every kk.
   const int wq0 = q0 + wave * 32;
   const int qrow = wq0 + r32;
   u32x4_t qf[KSTEPS], gf[KSTEPS];
+  float dsum = 0.0f;
 #pragma unroll
   for (int kk = 0; kk < KSTEPS; ++kk) {
     const uint32_t off = static_cast<uint32_t>(qrow) * ROWB + kk * 32 + half * 16;
     qf[kk] = buf_load16(rQ, off, 0) ^ p.qsign;
     gf[kk] = buf_load16(rG, off, 0);
+    const u32x4_t of = buf_load16(rO, off, 0);
+    const T* ov = reinterpret_cast<const T*>(&of);
+    const T* gv = reinterpret_cast<const T*>(&gf[kk]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      dsum = fmaf(static_cast<float>(ov[e]), static_cast<float>(gv[e]), dsum);
   }
-  const float lse2 = qrow < N ? p.lse[static_cast<size_t>(head) * N + qrow] * kLog2e : INFINITY;
-  const float Dq = qrow < N ? p.Dneg[static_cast<size_t>(head) * N + qrow] : 0.0f;  // -D
+  // D = dO . O over the whole row (the two halves of the wavefront hold its
+  // two halves); rows past N read as zeros.  The dK/dV pass, launched next on
+  // the same stream, starts its accumulators from -D and the row's score
+  // offset, written here once per row.
+  dsum = halves_sum(dsum);
+  const float lse = qrow < N ? p.lse[static_cast<size_t>(head) * N + qrow] : 0.0f;
+  if (half == 0 && qrow < N) {
+    p.Dneg[static_cast<size_t>(head) * N + qrow] = -dsum;
+    p.Loff[static_cast<size_t>(head) * N + qrow] = lse * p.lse_mul;
+  }
+  const float lse2 = qrow < N ? lse * kLog2e : INFINITY;
+  const float Dq = -dsum;
   const float c = p.c;
 
   f32x16_t acc[DBLK];
@@ -508,18 +502,11 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
 
 template <typename T, int D, int MASK>
 hipError_t launch_all(const BwdParams& p, hipStream_t stream) {
-  const int64_t rows = static_cast<int64_t>(p.n_heads) * p.N;
-  constexpr int rows_per_wg = 256 / (D / 8);
-  hipLaunchKernelGGL((bwd_rowdot_kernel<T, D>), dim3(static_cast<unsigned>(ceil_div(rows, rows_per_wg))),
-                     dim3(256), 0, stream, p, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-
   const int n_qblk = static_cast<int>(ceil_div(p.N, kBwdDqBlockQ));
   hipLaunchKernelGGL((bwd_dq_kernel<T, D, MASK>),
                      dim3(static_cast<unsigned>(static_cast<int64_t>(p.n_heads) * n_qblk)),
                      dim3(kBwdThreads), 0, stream, p, n_qblk);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
   const int n_kblk = static_cast<int>(ceil_div(p.N, kBwdKvBlockK));

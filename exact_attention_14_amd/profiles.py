@@ -38,7 +38,7 @@ def kernel_source_sha() -> str:
 
 
 def _demangle_short(name: str) -> str:
-    for key in ("fwd_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "bwd_rowdot_kernel"):
+    for key in ("fwd_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel"):
         if key in name:
             tail = name.split(key, 1)[1]
             return key + tail.split("EEvNS")[0].replace("IDF16b", "<bf16,").replace(
@@ -106,7 +106,7 @@ def traffic(fetch_dir: str, write_dir: str, workload: str, copy_mib: int, out_js
 
 def counters(counter_dir: str, kernel_stats: str, out_md: str, command: str,
              clock_ghz: float = 0.0) -> None:
-    keys = ("fwd_kernel", "bwd_rowdot_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel")
+    keys = ("fwd_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel")
     per = {}  # kernel -> counter -> dispatch -> value
     for path in glob.glob(os.path.join(counter_dir, "*counter_collection.csv")):
         for r in csv.DictReader(open(path)):
