@@ -16,13 +16,18 @@ Sources (cited as P1..P4 with their sections throughout this package):
   P4  ai6s.net/6a0ed07b662f9a54cb761aa2.html -- FlashAttention under the catlass
       templates (epilogue mask variants: none / causal / sliding window).
 
+Grouped-query heads and packed variable-length batches (P1 §5's
+extensions) are in ``grouped.py``.
+
 Every function here is pinned by ``tests/test_oracle_*.py`` against closed
 forms, invariants, brute force on tiny inputs and an independent library
 routine (torch's CPU float64 scaled-dot-product attention and autograd).
 """
 from .attention import (MASK_MODES, allowed_matrix, allowed_count, forward_head, forward_rows,
                         forward, backward_head, backward)
+from .grouped import (backward_gqa, backward_varlen, forward_gqa, forward_varlen, group_size)
 from .online import online_forward_head
 
 __all__ = ["MASK_MODES", "allowed_matrix", "allowed_count", "forward_head", "forward_rows",
-           "forward", "backward_head", "backward", "online_forward_head"]
+           "forward", "backward_head", "backward", "online_forward_head", "group_size",
+           "forward_gqa", "backward_gqa", "forward_varlen", "backward_varlen"]
