@@ -26,7 +26,8 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_E_NULLPTR", 2: "ATTN_E_SHAPE", 3: "ATTN_E_UNSUP
 # Every symbol include/attn.h declares.
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str",
            "attn_fwd_check", "attn_bwd_check", "attn_fwd_tiles", "attn_kv_tile_range",
-           "attn_fwd_workgroup", "attn_bwd_kv_workgroup")
+           "attn_fwd_workgroup", "attn_bwd_kv_workgroup", "attn_fwd_gqa", "attn_bwd_gqa",
+           "attn_fwd_varlen", "attn_bwd_varlen")
 
 
 class AttnError(RuntimeError):
@@ -55,6 +56,18 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd_check.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64,
                                  i64, f32, i32, i64, i64]
     L.attn_bwd_check.restype = i32
+    L.attn_fwd_gqa.argtypes = [i32, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32, i64, i64,
+                               vp]
+    L.attn_fwd_gqa.restype = i32
+    L.attn_bwd_gqa.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64,
+                               i64, f32, i32, i64, i64, vp]
+    L.attn_bwd_gqa.restype = i32
+    L.attn_fwd_varlen.argtypes = [i32, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, f32,
+                                  i32, i64, i64, vp]
+    L.attn_fwd_varlen.restype = i32
+    L.attn_bwd_varlen.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, i64, i64,
+                                  i64, i64, i64, i64, f32, i32, i64, i64, vp]
+    L.attn_bwd_varlen.restype = i32
     L.attn_bwd_workspace_bytes.argtypes = [i32, i64, i64, i64, i64]
     L.attn_bwd_workspace_bytes.restype = sz
     L.attn_status_str.argtypes = [i32]
@@ -112,6 +125,17 @@ def _check4(name: str, t: torch.Tensor, ref: torch.Tensor):
         raise ValueError(f"{name} must be contiguous [B, H, N, d]")
 
 
+def _check_kv(name: str, t: torch.Tensor, q: torch.Tensor, ref: torch.Tensor):
+    """K, V (and dK, dV) have q's shape except for the head count, that of ``ref``."""
+    want = (q.shape[0], ref.shape[1]) + tuple(q.shape[2:])
+    if t.dim() != 4 or tuple(t.shape) != want:
+        raise ValueError(f"{name} must have shape {want}, got {tuple(t.shape)}")
+    if t.dtype != q.dtype or t.device != q.device:
+        raise ValueError(f"{name} must be {q.dtype} on {q.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
 def _stream_ptr(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
@@ -130,18 +154,21 @@ def _check_lse(lse: torch.Tensor, q: torch.Tensor):
 
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, mask=None, scale=None,
              out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
-    """Forward pass; returns (O, lse).  Inputs: contiguous [B, H, N, d] on a GPU.
+    """Forward pass; returns (O, lse).  Inputs: contiguous q [B, H, N, d] and k, v
+    [B, H_kv, N, d] on a GPU (H_kv < H: grouped-query attention, query head h
+    reads key/value head h // (H // H_kv)).
 
     ``scale`` defaults to 1/sqrt(d) (P1 §1).  ``out``/``lse`` may be given to
     write into preallocated buffers.
     """
-    if q.dim() != 4:
-        raise ValueError("q must be [B, H, N, d]")
-    _check4("k", k, q)
-    _check4("v", v, q)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, H, N, d] and k [B, H_kv, N, d]")
     _check4("q", q, q)
+    _check_kv("k", k, q, k)
+    _check_kv("v", v, q, k)
     _check_gpu(q)
     B, H, N, d = q.shape
+    H_kv = k.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     mode, wl, wr = mask_args(mask)
@@ -156,10 +183,17 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, mask=None, sc
         _check_lse(lse, q)
     # The library launches on the calling thread's current device.
     with torch.cuda.device(q.device):
-        st = lib().attn_fwd(dt, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                            lse.data_ptr(), B, H, N, d, float(scale), mode, wl, wr,
-                            _stream_ptr(q.device))
-    _raise("attn_fwd", st)
+        if H_kv == H:
+            fn = "attn_fwd"
+            st = lib().attn_fwd(dt, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                lse.data_ptr(), B, H, N, d, float(scale), mode, wl, wr,
+                                _stream_ptr(q.device))
+        else:
+            fn = "attn_fwd_gqa"
+            st = lib().attn_fwd_gqa(dt, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                    lse.data_ptr(), B, H, H_kv, N, d, float(scale), mode, wl, wr,
+                                    _stream_ptr(q.device))
+    _raise(fn, st)
     return out, lse
 
 
@@ -169,15 +203,22 @@ def attn_bwd_workspace_bytes(dtype: torch.dtype, B: int, H: int, N: int, d: int)
 
 
 def attn_bwd(q, k, v, o, lse, do, *, mask=None, scale=None, workspace=None):
-    """Recomputation backward; returns (dQ, dK, dV) for upstream gradient ``do``."""
-    if q.dim() != 4:
-        raise ValueError("q must be [B, H, N, d]")
+    """Recomputation backward; returns (dQ, dK, dV) for upstream gradient ``do``.
+
+    k, v (and the returned dK, dV) may have fewer heads than q (grouped-query
+    attention); dK, dV then sum over each key/value head's query heads.
+    """
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, H, N, d] and k [B, H_kv, N, d]")
     _check4("q", q, q)
-    for name, t in (("k", k), ("v", v), ("o", o), ("do", do)):
+    for name, t in (("o", o), ("do", do)):
         _check4(name, t, q)
+    _check_kv("k", k, q, k)
+    _check_kv("v", v, q, k)
     _check_gpu(q)
     _check_lse(lse, q)
     B, H, N, d = q.shape
+    H_kv = k.shape[1]
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     mode, wl, wr = mask_args(mask)
@@ -188,13 +229,115 @@ def attn_bwd(q, k, v, o, lse, do, *, mask=None, scale=None, workspace=None):
     elif workspace.device != q.device or not workspace.is_contiguous():
         raise ValueError(f"workspace must be a contiguous tensor on {q.device}")
     ws_bytes = workspace.numel() * workspace.element_size()
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     with torch.cuda.device(q.device):
-        st = lib().attn_bwd(dt, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                            lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                            dv.data_ptr(), workspace.data_ptr(), ws_bytes, B, H, N, d,
-                            float(scale), mode, wl, wr, _stream_ptr(q.device))
-    _raise("attn_bwd", st)
+        if H_kv == H:
+            fn = "attn_bwd"
+            st = lib().attn_bwd(dt, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                dv.data_ptr(), workspace.data_ptr(), ws_bytes, B, H, N, d,
+                                float(scale), mode, wl, wr, _stream_ptr(q.device))
+        else:
+            fn = "attn_bwd_gqa"
+            st = lib().attn_bwd_gqa(dt, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                    lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                    dv.data_ptr(), workspace.data_ptr(), ws_bytes, B, H, H_kv, N,
+                                    d, float(scale), mode, wl, wr, _stream_ptr(q.device))
+    _raise(fn, st)
+    return dq, dk, dv
+
+
+def _check_packed(q, k, v):
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("packed q must be [H, T, d] and k, v [H_kv, T, d]")
+    H, T, d = q.shape
+    for name, t in (("k", k), ("v", v)):
+        if tuple(t.shape) != (k.shape[0], T, d) or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must be {q.dtype} [H_kv, {T}, {d}] on {q.device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    return H, k.shape[0], T, d
+
+
+def _check_offsets(cu_seqlens, q):
+    if (cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2 or cu_seqlens.dtype != torch.int32
+            or cu_seqlens.device != q.device or not cu_seqlens.is_contiguous()):
+        raise ValueError(f"cu_seqlens must be a contiguous int32 vector of n_seqs + 1 row offsets "
+                         f"on {q.device}")
+    return cu_seqlens.numel() - 1
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens, max_seqlen: int, *, mask=None, scale=None, out=None,
+                    lse=None):
+    """Forward over a packed variable-length batch; returns (O [H, T, d], lse [H, T]).
+
+    q: [H, T, d]; k, v: [H_kv, T, d]; sequence s is rows cu_seqlens[s] ..
+    cu_seqlens[s+1] - 1 and attends only to itself (masks count positions from
+    its first row).  ``max_seqlen`` must be at least every sequence's length.
+    Rows outside every sequence are left as they are in ``out`` / ``lse``.
+    """
+    H, H_kv, T, d = _check_packed(q, k, v)
+    _check_gpu(q)
+    n_seqs = _check_offsets(cu_seqlens, q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    mode, wl, wr = mask_args(mask)
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    elif tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError(f"out must be contiguous {q.dtype} {tuple(q.shape)}")
+    if lse is None:
+        lse = torch.empty((H, T), dtype=torch.float32, device=q.device)
+    elif (tuple(lse.shape) != (H, T) or lse.dtype != torch.float32 or not lse.is_contiguous()
+          or lse.device != q.device):
+        raise ValueError(f"lse must be contiguous float32 [H, T] on {q.device}")
+    with torch.cuda.device(q.device):
+        st = lib().attn_fwd_varlen(dt, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                   lse.data_ptr(), cu_seqlens.data_ptr(), n_seqs, int(max_seqlen),
+                                   T, H, H_kv, d, float(scale), mode, wl, wr,
+                                   _stream_ptr(q.device))
+    _raise("attn_fwd_varlen", st)
+    return out, lse
+
+
+def attn_bwd_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen: int, *, mask=None, scale=None,
+                    workspace=None):
+    """Backward over a packed variable-length batch; returns (dQ, dK, dV).
+
+    Shapes as for attn_fwd_varlen; o and do are [H, T, d], lse [H, T].  Rows
+    outside every sequence of the returned tensors are unspecified.
+    """
+    H, H_kv, T, d = _check_packed(q, k, v)
+    _check_gpu(q)
+    for name, t in (("o", o), ("do", do)):
+        if tuple(t.shape) != tuple(q.shape) or t.dtype != q.dtype or not t.is_contiguous() \
+                or t.device != q.device:
+            raise ValueError(f"{name} must be contiguous {q.dtype} {tuple(q.shape)} on {q.device}")
+    if (tuple(lse.shape) != (H, T) or lse.dtype != torch.float32 or not lse.is_contiguous()
+            or lse.device != q.device):
+        raise ValueError(f"lse must be contiguous float32 [H, T] on {q.device}")
+    n_seqs = _check_offsets(cu_seqlens, q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    mode, wl, wr = mask_args(mask)
+    dt = _dtype_code(q)
+    need = attn_bwd_workspace_bytes(q.dtype, 1, H, T, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    elif workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous tensor on {q.device}")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    with torch.cuda.device(q.device):
+        st = lib().attn_bwd_varlen(dt, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                   lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                   dv.data_ptr(), workspace.data_ptr(), ws_bytes,
+                                   cu_seqlens.data_ptr(), n_seqs, int(max_seqlen), T, H, H_kv, d,
+                                   float(scale), mode, wl, wr, _stream_ptr(q.device))
+    _raise("attn_bwd_varlen", st)
     return dq, dk, dv
 
 

@@ -140,17 +140,22 @@ void bwd_dq_kernel(BwdParams p, int n_qblk) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, half = lane >> 5, r32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int N = p.N;
   int64_t head, qblk;
   fwd_work_item(blockIdx.x, p.n_heads, n_qblk, MASK, &head, &qblk);
+  // The query head's rows (a packed sequence's blocks past its end exit) and
+  // its key/value head.
+  const HeadRows hr = query_rows(p.g, head);
+  const int N = static_cast<int>(hr.len);
   const int q0 = static_cast<int>(qblk) * BQ;
-  const size_t hoff = static_cast<size_t>(head) * N * D * 2;
+  if (q0 >= N) return;
+  const size_t qoff = static_cast<size_t>(hr.q_row0) * ROWB;
+  const size_t kvoff = static_cast<size_t>(hr.kv_row0) * ROWB;
   const uint32_t head_bytes = static_cast<uint32_t>(N) * ROWB;
-  const auto rQ = make_rsrc(reinterpret_cast<const char*>(p.Q) + hoff, head_bytes);
-  const auto rK = make_rsrc(reinterpret_cast<const char*>(p.K) + hoff, head_bytes);
-  const auto rV = make_rsrc(reinterpret_cast<const char*>(p.V) + hoff, head_bytes);
-  const auto rG = make_rsrc(reinterpret_cast<const char*>(p.dO) + hoff, head_bytes);
-  const auto rO = make_rsrc(reinterpret_cast<const char*>(p.O) + hoff, head_bytes);
+  const auto rQ = make_rsrc(reinterpret_cast<const char*>(p.Q) + qoff, head_bytes);
+  const auto rK = make_rsrc(reinterpret_cast<const char*>(p.K) + kvoff, head_bytes);
+  const auto rV = make_rsrc(reinterpret_cast<const char*>(p.V) + kvoff, head_bytes);
+  const auto rG = make_rsrc(reinterpret_cast<const char*>(p.dO) + qoff, head_bytes);
+  const auto rO = make_rsrc(reinterpret_cast<const char*>(p.O) + qoff, head_bytes);
 
   // Q and dO of this lane's row stay in registers (B operands); the lane
   // holds elements kk*16 + half*8 .. +7 of the row for every kk.
@@ -175,10 +180,11 @@ void bwd_dq_kernel(BwdParams p, int n_qblk) {
   // the same stream, starts its accumulators from -D and the row's score
   // offset, written here once per row.
   dsum = halves_sum(dsum);
-  const float lse = qrow < N ? p.lse[static_cast<size_t>(head) * N + qrow] : 0.0f;
+  const size_t srow = static_cast<size_t>(hr.q_row0) + qrow;
+  const float lse = qrow < N ? p.lse[srow] : 0.0f;
   if (half == 0 && qrow < N) {
-    p.Dneg[static_cast<size_t>(head) * N + qrow] = -dsum;
-    p.Loff[static_cast<size_t>(head) * N + qrow] = lse * p.lse_mul;
+    p.Dneg[srow] = -dsum;
+    p.Loff[srow] = lse * p.lse_mul;
   }
   const float lse2 = qrow < N ? lse * kLog2e : INFINITY;
   const float Dq = -dsum;
@@ -266,7 +272,7 @@ void bwd_dq_kernel(BwdParams p, int n_qblk) {
   }
 
   // dQ = scale * dS K; stores past N are dropped by the buffer bound.
-  const auto rdQ = make_rsrc(reinterpret_cast<char*>(p.dQ) + hoff, head_bytes);
+  const auto rdQ = make_rsrc(reinterpret_cast<char*>(p.dQ) + qoff, head_bytes);
   const float sc = p.scale;
 #pragma unroll
   for (int db = 0; db < DBLK; ++db)
@@ -297,18 +303,18 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, half = lane >> 5, r32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int N = p.N;
   int64_t head, kblk;
-  kv_work_item(blockIdx.x, p.n_heads, n_kblk, MASK, &head, &kblk);
+  kv_work_item(blockIdx.x, p.n_kv_heads, n_kblk, MASK, &head, &kblk);
+  // The key/value head's rows (a packed sequence's blocks past its end exit)
+  // and its group of query heads, whose contributions all accumulate here.
+  const KvHeadRows kr = kv_rows(p.g, head);
+  const int N = static_cast<int>(kr.len);
   const int k0 = static_cast<int>(kblk) * BK;
-  const size_t hoff = static_cast<size_t>(head) * N * D * 2;
+  if (k0 >= N) return;
+  const size_t kvoff = static_cast<size_t>(kr.kv_row0) * ROWB;
   const uint32_t head_bytes = static_cast<uint32_t>(N) * ROWB;
-  const auto rQ = make_rsrc(reinterpret_cast<const char*>(p.Q) + hoff, head_bytes);
-  const auto rK = make_rsrc(reinterpret_cast<const char*>(p.K) + hoff, head_bytes);
-  const auto rV = make_rsrc(reinterpret_cast<const char*>(p.V) + hoff, head_bytes);
-  const auto rG = make_rsrc(reinterpret_cast<const char*>(p.dO) + hoff, head_bytes);
-  const auto rL = make_rsrc(p.Loff + static_cast<size_t>(head) * N, static_cast<uint32_t>(N) * 4);
-  const auto rD = make_rsrc(p.Dneg + static_cast<size_t>(head) * N, static_cast<uint32_t>(N) * 4);
+  const auto rK = make_rsrc(reinterpret_cast<const char*>(p.K) + kvoff, head_bytes);
+  const auto rV = make_rsrc(reinterpret_cast<const char*>(p.V) + kvoff, head_bytes);
 
   // K (with a negative scale's sign flip folded in) and V as B operands of
   // S = Q K^T and dP = dO V^T: lane (key r32 of block kb, half).
@@ -347,7 +353,8 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
   // The score offsets and -D of a query tile (the starting values of the
   // score and dP accumulators), one 4-byte direct load each by wavefront 0;
   // rows past N read as zero and are masked.
-  auto load_stats = [&](int q0, float* sl, float* sd) {
+  auto load_stats = [&](__amdgpu_buffer_rsrc_t rL, __amdgpu_buffer_rsrc_t rD, int q0, float* sl,
+                        float* sd) {
     if (wave == 0) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rL, (__attribute__((address_space(3))) void*)(sl), 4,
                                                lane * 4, q0 * 4, 0, 0);
@@ -449,29 +456,40 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
     }
   };
 
-  ld.load(rQ, q_lds0, lo * BQ);
-  ld.load(rG, g_lds0, lo * BQ);
-  load_stats(lo * BQ, s_off0, s_dn0);
-  wait_vmem();
-  __syncthreads();
-  for (int t = lo; t < hi; t += 2) {
-    if (t + 1 < hi) {
-      ld.load(rQ, q_lds1, (t + 1) * BQ);
-      ld.load(rG, g_lds1, (t + 1) * BQ);
-      load_stats((t + 1) * BQ, s_off1, s_dn1);
-    }
-    tile(t, q_lds0, g_lds0, s_off0, s_dn0);
+  // The query tiles of each query head of the group in turn (one head
+  // without grouping); every tile ends with a barrier, so the next head's
+  // first loads may refill stage 0.
+  for (int gq = 0; gq < p.g.group; ++gq) {
+    const size_t qoff = static_cast<size_t>(kr.q_row0 + gq * kr.q_stride) * ROWB;
+    const size_t soff = static_cast<size_t>(kr.q_row0 + gq * kr.q_stride);
+    const auto rQ = make_rsrc(reinterpret_cast<const char*>(p.Q) + qoff, head_bytes);
+    const auto rG = make_rsrc(reinterpret_cast<const char*>(p.dO) + qoff, head_bytes);
+    const auto rL = make_rsrc(p.Loff + soff, static_cast<uint32_t>(N) * 4);
+    const auto rD = make_rsrc(p.Dneg + soff, static_cast<uint32_t>(N) * 4);
+    ld.load(rQ, q_lds0, lo * BQ);
+    ld.load(rG, g_lds0, lo * BQ);
+    load_stats(rL, rD, lo * BQ, s_off0, s_dn0);
     wait_vmem();
     __syncthreads();
-    if (t + 1 >= hi) break;
-    if (t + 2 < hi) {
-      ld.load(rQ, q_lds0, (t + 2) * BQ);
-      ld.load(rG, g_lds0, (t + 2) * BQ);
-      load_stats((t + 2) * BQ, s_off0, s_dn0);
+    for (int t = lo; t < hi; t += 2) {
+      if (t + 1 < hi) {
+        ld.load(rQ, q_lds1, (t + 1) * BQ);
+        ld.load(rG, g_lds1, (t + 1) * BQ);
+        load_stats(rL, rD, (t + 1) * BQ, s_off1, s_dn1);
+      }
+      tile(t, q_lds0, g_lds0, s_off0, s_dn0);
+      wait_vmem();
+      __syncthreads();
+      if (t + 1 >= hi) break;
+      if (t + 2 < hi) {
+        ld.load(rQ, q_lds0, (t + 2) * BQ);
+        ld.load(rG, g_lds0, (t + 2) * BQ);
+        load_stats(rL, rD, (t + 2) * BQ, s_off0, s_dn0);
+      }
+      tile(t + 1, q_lds1, g_lds1, s_off1, s_dn1);
+      wait_vmem();
+      __syncthreads();
     }
-    tile(t + 1, q_lds1, g_lds1, s_off1, s_dn1);
-    wait_vmem();
-    __syncthreads();
   }
 
   // K entered the products with a negative scale's sign flip, so
@@ -479,8 +497,8 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
   acc_fence(dv);
   acc_fence(dk);
   const float sc = p.scale;
-  const auto rdK = make_rsrc(reinterpret_cast<char*>(p.dK) + hoff, head_bytes);
-  const auto rdV = make_rsrc(reinterpret_cast<char*>(p.dV) + hoff, head_bytes);
+  const auto rdK = make_rsrc(reinterpret_cast<char*>(p.dK) + kvoff, head_bytes);
+  const auto rdV = make_rsrc(reinterpret_cast<char*>(p.dV) + kvoff, head_bytes);
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -502,16 +520,16 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
 
 template <typename T, int D, int MASK>
 hipError_t launch_all(const BwdParams& p, hipStream_t stream) {
-  const int n_qblk = static_cast<int>(ceil_div(p.N, kBwdDqBlockQ));
+  const int n_qblk = static_cast<int>(ceil_div(p.max_len, kBwdDqBlockQ));
   hipLaunchKernelGGL((bwd_dq_kernel<T, D, MASK>),
                      dim3(static_cast<unsigned>(static_cast<int64_t>(p.n_heads) * n_qblk)),
                      dim3(kBwdThreads), 0, stream, p, n_qblk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  const int n_kblk = static_cast<int>(ceil_div(p.N, kBwdKvBlockK));
+  const int n_kblk = static_cast<int>(ceil_div(p.max_len, kBwdKvBlockK));
   hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, MASK>),
-                     dim3(static_cast<unsigned>(static_cast<int64_t>(p.n_heads) * n_kblk)),
+                     dim3(static_cast<unsigned>(static_cast<int64_t>(p.n_kv_heads) * n_kblk)),
                      dim3(kBwdThreads), 0, stream, p, n_kblk);
   return hipGetLastError();
 }

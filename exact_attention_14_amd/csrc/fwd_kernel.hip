@@ -105,16 +105,22 @@ void fwd_kernel(FwdParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, half = lane >> 5, r32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wavefront
-  const int N = p.N;
 
   int64_t head, qblk;
   fwd_work_item(blockIdx.x, p.n_heads, p.n_qblk, MASK, &head, &qblk);
+  // The head's rows: all N of a fixed-length batch, or one packed sequence
+  // (whose query blocks past its end have nothing to do).  K and V come from
+  // the head's key/value head.
+  const HeadRows hr = query_rows(p.g, head);
+  const int N = static_cast<int>(hr.len);
   const int q0 = static_cast<int>(qblk) * BR;
-  const size_t hoff = static_cast<size_t>(head) * N * D * 2;
+  if (q0 >= N) return;
+  const size_t qoff = static_cast<size_t>(hr.q_row0) * ROW_BYTES;
+  const size_t kvoff = static_cast<size_t>(hr.kv_row0) * ROW_BYTES;
   const uint32_t head_bytes = static_cast<uint32_t>(N) * ROW_BYTES;
-  const auto rQ = make_rsrc(reinterpret_cast<const char*>(p.Q) + hoff, head_bytes);
-  const auto rK = make_rsrc(reinterpret_cast<const char*>(p.K) + hoff, head_bytes);
-  const auto rV = make_rsrc(reinterpret_cast<const char*>(p.V) + hoff, head_bytes);
+  const auto rQ = make_rsrc(reinterpret_cast<const char*>(p.Q) + qoff, head_bytes);
+  const auto rK = make_rsrc(reinterpret_cast<const char*>(p.K) + kvoff, head_bytes);
+  const auto rV = make_rsrc(reinterpret_cast<const char*>(p.V) + kvoff, head_bytes);
 
   int64_t lo64, hi64;
   kv_tile_range(N, q0, BR, BC, MASK, p.wl, p.wr, &lo64, &hi64);
@@ -380,7 +386,7 @@ void fwd_kernel(FwdParams p) {
   const float lt = halves_sum(l);
   const float lrt = kOneSum ? lt : halves_sum(lr);
   const float inv = 1.0f / lrt;
-  const auto rO = make_rsrc(reinterpret_cast<char*>(p.O) + hoff, head_bytes);
+  const auto rO = make_rsrc(reinterpret_cast<char*>(p.O) + qoff, head_bytes);
 #pragma unroll
   for (int db = 0; db < DBLK; ++db) {
 #pragma unroll
@@ -390,7 +396,7 @@ void fwd_kernel(FwdParams p) {
       buf_store8(v, rO, static_cast<uint32_t>(qrow) * ROW_BYTES + (db * 32 + g * 8 + half * 4) * 2);
     }
   }
-  const auto rL = make_rsrc(p.lse + static_cast<size_t>(head) * N, static_cast<uint32_t>(N) * 4);
+  const auto rL = make_rsrc(p.lse + hr.q_row0, static_cast<uint32_t>(N) * 4);
   buf_store4((m + log2f(lt)) * kLn2, rL, static_cast<uint32_t>(qrow) * 4);
 }
 

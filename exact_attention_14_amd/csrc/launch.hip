@@ -1,4 +1,5 @@
-// launch.hip -- the C ABI entry points that enqueue work (attn_fwd, attn_bwd).
+// launch.hip -- the C ABI entry points that enqueue work: attn_fwd / attn_bwd and
+// their grouped-query (_gqa) and packed variable-length (_varlen) variants.
 // Validation lives in validate.cpp and runs before any HIP call.
 #include <hip/hip_runtime.h>
 
@@ -24,6 +25,72 @@ float exp2_coeff(float scale) {
 
 int clip_window(int64_t w, int64_t N) { return static_cast<int>(w < N ? w : N); }
 
+HeadGeom head_geom(const Geometry& g, const int32_t* cu_seqlens) {
+  HeadGeom h{};
+  h.rows = static_cast<int>(g.rows);
+  h.H = static_cast<int>(g.H);
+  h.group = static_cast<int>(g.H / g.H_kv);
+  h.cu_seqlens = g.packed ? cu_seqlens : nullptr;
+  return h;
+}
+
+// Windows are read only for a sliding mask and act as unbounded from the
+// head's row count on (for a packed batch, from T on: every sequence is
+// shorter).
+attn_status fwd_impl(attn_dtype dt, const void* Q, const void* K, const void* V, void* O,
+                     float* lse, const int32_t* cu_seqlens, const Geometry& g, float scale,
+                     attn_mask_mode mode, int64_t wl, int64_t wr, void* stream) {
+  attn_status s = fwd_check_g(dt, Q, K, V, O, lse, cu_seqlens, g, scale, mode, wl, wr);
+  if (s != ATTN_OK) return s;
+  FwdParams p{};
+  p.Q = Q; p.K = K; p.V = V; p.O = O; p.lse = lse;
+  p.g = head_geom(g, cu_seqlens);
+  p.n_heads = static_cast<int>(g.n_heads());
+  p.n_qblk = static_cast<int>(ceil_div(g.max_len, fwd_block_q(mode)));
+  p.wl = mode == ATTN_MASK_SLIDING ? clip_window(wl, g.rows) : 0;
+  p.wr = mode == ATTN_MASK_SLIDING ? clip_window(wr, g.rows) : 0;
+  p.c = exp2_coeff(scale);
+  p.qsign = scale < 0.0f ? 0x80008000u : 0u;
+  const int64_t n_wg = g.n_heads() * p.n_qblk;
+  hipError_t e = launch_fwd(p, dt == ATTN_BF16, static_cast<int>(g.d), mode, n_wg,
+                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
+attn_status bwd_impl(attn_dtype dt, const void* Q, const void* K, const void* V, const void* O,
+                     const float* lse, const void* dO, void* dQ, void* dK, void* dV,
+                     void* workspace, size_t workspace_bytes, const int32_t* cu_seqlens,
+                     const Geometry& g, float scale, attn_mask_mode mode, int64_t wl, int64_t wr,
+                     void* stream) {
+  attn_status s = bwd_check_g(dt, Q, K, V, O, lse, dO, dQ, dK, dV, workspace, workspace_bytes,
+                              cu_seqlens, g, scale, mode, wl, wr);
+  if (s != ATTN_OK) return s;
+  BwdParams p{};
+  p.Q = Q; p.K = K; p.V = V; p.O = O; p.lse = lse; p.dO = dO;
+  p.dQ = dQ; p.dK = dK; p.dV = dV;
+  p.Dneg = static_cast<float*>(workspace);
+  p.Loff = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                    row_array_bytes(1, 1, g.q_rows()));
+  p.g = head_geom(g, cu_seqlens);
+  p.n_heads = static_cast<int>(g.n_heads());
+  p.n_kv_heads = static_cast<int>(g.n_kv_heads());
+  p.max_len = static_cast<int>(g.max_len);
+  p.wl = mode == ATTN_MASK_SLIDING ? clip_window(wl, g.rows) : 0;
+  p.wr = mode == ATTN_MASK_SLIDING ? clip_window(wr, g.rows) : 0;
+  p.c = exp2_coeff(scale);
+  p.scale = scale;
+  p.qsign = scale < 0.0f ? 0x80008000u : 0u;
+  p.lse_mul = -1.4426950408889634f / p.c;
+  hipError_t e = launch_bwd(p, dt == ATTN_BF16, static_cast<int>(g.d), mode,
+                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+}
+
+Geometry packed_geometry(int64_t n_seqs, int64_t max_seqlen, int64_t total, int64_t H,
+                         int64_t H_kv, int64_t d) {
+  return Geometry{n_seqs, H, H_kv, total, max_seqlen, d, true};
+}
+
 }  // namespace
 }  // namespace attn
 
@@ -33,22 +100,26 @@ attn_status attn_fwd(attn_dtype dt, const void* Q, const void* K, const void* V,
                      float* lse, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
                      attn_mask_mode mode, int64_t window_left, int64_t window_right,
                      void* stream) {
-  attn_status s = attn::fwd_check(dt, Q, K, V, O, lse, B, H, N, d, scale, mode, window_left,
-                                  window_right);
-  if (s != ATTN_OK) return s;
-  attn::FwdParams p{};
-  p.Q = Q; p.K = K; p.V = V; p.O = O; p.lse = lse;
-  p.N = static_cast<int>(N);
-  p.n_heads = static_cast<int>(B * H);
-  p.n_qblk = static_cast<int>(attn::ceil_div(N, attn::fwd_block_q(mode)));
-  p.wl = mode == ATTN_MASK_SLIDING ? attn::clip_window(window_left, N) : 0;
-  p.wr = mode == ATTN_MASK_SLIDING ? attn::clip_window(window_right, N) : 0;
-  p.c = attn::exp2_coeff(scale);
-  p.qsign = scale < 0.0f ? 0x80008000u : 0u;
-  const int64_t n_wg = B * H * p.n_qblk;
-  hipError_t e = attn::launch_fwd(p, dt == ATTN_BF16, static_cast<int>(d), mode, n_wg,
-                                  static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+  return attn::fwd_impl(dt, Q, K, V, O, lse, nullptr, attn::fixed_geometry(B, H, H, N, d), scale,
+                        mode, window_left, window_right, stream);
+}
+
+attn_status attn_fwd_gqa(attn_dtype dt, const void* Q, const void* K, const void* V, void* O,
+                         float* lse, int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d,
+                         float scale, attn_mask_mode mode, int64_t window_left,
+                         int64_t window_right, void* stream) {
+  return attn::fwd_impl(dt, Q, K, V, O, lse, nullptr, attn::fixed_geometry(B, H, H_kv, N, d),
+                        scale, mode, window_left, window_right, stream);
+}
+
+attn_status attn_fwd_varlen(attn_dtype dt, const void* Q, const void* K, const void* V, void* O,
+                            float* lse, const int32_t* cu_seqlens, int64_t n_seqs,
+                            int64_t max_seqlen, int64_t total, int64_t H, int64_t H_kv,
+                            int64_t d, float scale, attn_mask_mode mode, int64_t window_left,
+                            int64_t window_right, void* stream) {
+  return attn::fwd_impl(dt, Q, K, V, O, lse, cu_seqlens,
+                        attn::packed_geometry(n_seqs, max_seqlen, total, H, H_kv, d), scale,
+                        mode, window_left, window_right, stream);
 }
 
 attn_status attn_bwd(attn_dtype dt, const void* Q, const void* K, const void* V, const void* O,
@@ -56,26 +127,31 @@ attn_status attn_bwd(attn_dtype dt, const void* Q, const void* K, const void* V,
                      void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t N,
                      int64_t d, float scale, attn_mask_mode mode, int64_t window_left,
                      int64_t window_right, void* stream) {
-  attn_status s = attn::bwd_check(dt, Q, K, V, O, lse, dO, dQ, dK, dV, workspace, workspace_bytes,
-                                  B, H, N, d, scale, mode, window_left, window_right);
-  if (s != ATTN_OK) return s;
-  attn::BwdParams p{};
-  p.Q = Q; p.K = K; p.V = V; p.O = O; p.lse = lse; p.dO = dO;
-  p.dQ = dQ; p.dK = dK; p.dV = dV;
-  p.Dneg = static_cast<float*>(workspace);
-  p.Loff = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                    attn::row_array_bytes(B, H, N));
-  p.N = static_cast<int>(N);
-  p.n_heads = static_cast<int>(B * H);
-  p.wl = mode == ATTN_MASK_SLIDING ? attn::clip_window(window_left, N) : 0;
-  p.wr = mode == ATTN_MASK_SLIDING ? attn::clip_window(window_right, N) : 0;
-  p.c = attn::exp2_coeff(scale);
-  p.scale = scale;
-  p.qsign = scale < 0.0f ? 0x80008000u : 0u;
-  p.lse_mul = -1.4426950408889634f / p.c;
-  hipError_t e = attn::launch_bwd(p, dt == ATTN_BF16, static_cast<int>(d), mode,
-                                  static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
+  return attn::bwd_impl(dt, Q, K, V, O, lse, dO, dQ, dK, dV, workspace, workspace_bytes, nullptr,
+                        attn::fixed_geometry(B, H, H, N, d), scale, mode, window_left,
+                        window_right, stream);
+}
+
+attn_status attn_bwd_gqa(attn_dtype dt, const void* Q, const void* K, const void* V,
+                         const void* O, const float* lse, const void* dO, void* dQ, void* dK,
+                         void* dV, void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                         int64_t H_kv, int64_t N, int64_t d, float scale, attn_mask_mode mode,
+                         int64_t window_left, int64_t window_right, void* stream) {
+  return attn::bwd_impl(dt, Q, K, V, O, lse, dO, dQ, dK, dV, workspace, workspace_bytes, nullptr,
+                        attn::fixed_geometry(B, H, H_kv, N, d), scale, mode, window_left,
+                        window_right, stream);
+}
+
+attn_status attn_bwd_varlen(attn_dtype dt, const void* Q, const void* K, const void* V,
+                            const void* O, const float* lse, const void* dO, void* dQ, void* dK,
+                            void* dV, void* workspace, size_t workspace_bytes,
+                            const int32_t* cu_seqlens, int64_t n_seqs, int64_t max_seqlen,
+                            int64_t total, int64_t H, int64_t H_kv, int64_t d, float scale,
+                            attn_mask_mode mode, int64_t window_left, int64_t window_right,
+                            void* stream) {
+  return attn::bwd_impl(dt, Q, K, V, O, lse, dO, dQ, dK, dV, workspace, workspace_bytes,
+                        cu_seqlens, attn::packed_geometry(n_seqs, max_seqlen, total, H, H_kv, d),
+                        scale, mode, window_left, window_right, stream);
 }
 
 }  // extern "C"

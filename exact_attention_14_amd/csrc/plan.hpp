@@ -113,6 +113,69 @@ ATTN_HD bool tile_none_allowed(int64_t N, int64_t q0, int64_t nq, int64_t k0, in
   return false;
 }
 
+// Query heads and their rows.  A launch's query heads are numbered
+// x = outer * H + h, where outer is the batch index (fixed-length batches,
+// [B, H, N, d]) or the sequence index (packed variable-length batches,
+// [H, T, d]), and h the query head.  Query head h reads key/value head
+// h / group (group = H / H_kv query heads share one; group = 1 is standard
+// multi-head attention, H_kv = 1 multi-query attention), so a fixed-length
+// query head x = b*H + h reads key/value head b*H_kv + h/group, and the
+// query heads of one key/value head are consecutive.  q_row0 / kv_row0 are
+// the indices of the head's first row in the [rows, d] view of the query
+// side (Q, O, dO, dQ and the per-row lse and workspace arrays) and of the
+// key/value side (K, V, dK, dV); len is the head's row count.  For a packed
+// batch, seq_lo/seq_hi are the sequence's row offsets, which the caller
+// supplies and which are clamped here to 0 <= seq_lo <= seq_hi <= rows, so
+// a head never reaches outside its tensors whatever the offsets hold.
+struct HeadRows {
+  int64_t q_row0, kv_row0, len;
+};
+
+ATTN_HD HeadRows query_head_rows(int64_t x, int64_t H, int64_t group, int64_t rows, bool packed,
+                                 int64_t seq_lo, int64_t seq_hi) {
+  const int64_t outer = x / H, h = x % H, kvh = h / group, H_kv = H / group;
+  HeadRows r;
+  if (!packed) {
+    r.q_row0 = x * rows;
+    r.kv_row0 = (outer * H_kv + kvh) * rows;
+    r.len = rows;
+  } else {
+    const int64_t lo = imin(imax(seq_lo, 0), rows);
+    const int64_t hi = imin(imax(seq_hi, lo), rows);
+    r.q_row0 = h * rows + lo;
+    r.kv_row0 = kvh * rows + lo;
+    r.len = hi - lo;
+  }
+  return r;
+}
+
+// Key/value head y = outer * H_kv + kvh of the backward's key-major pass and
+// its group of query heads: query head kvh*group + g (g < group) starts at
+// row q_row0 + g * q_stride of the query side.
+struct KvHeadRows {
+  int64_t kv_row0, q_row0, q_stride, len;
+};
+
+ATTN_HD KvHeadRows kv_head_rows(int64_t y, int64_t H_kv, int64_t group, int64_t rows, bool packed,
+                                int64_t seq_lo, int64_t seq_hi) {
+  const int64_t outer = y / H_kv, kvh = y % H_kv, H = H_kv * group;
+  KvHeadRows r;
+  if (!packed) {
+    r.kv_row0 = y * rows;
+    r.q_row0 = (outer * H + kvh * group) * rows;
+    r.q_stride = rows;
+    r.len = rows;
+  } else {
+    const int64_t lo = imin(imax(seq_lo, 0), rows);
+    const int64_t hi = imin(imax(seq_hi, lo), rows);
+    r.kv_row0 = kvh * rows + lo;
+    r.q_row0 = kvh * group * rows + lo;
+    r.q_stride = rows;
+    r.len = hi - lo;
+  }
+  return r;
+}
+
 // Workgroup id -> work item.  The hardware deals consecutive workgroup ids
 // round-robin to the kNumXcd dies; this bijection gives die x a contiguous
 // run of work items, so all query blocks of a head share one die's L2.

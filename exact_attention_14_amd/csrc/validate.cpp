@@ -22,11 +22,7 @@ bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Byte size of an [B, H, N, d] tensor of 2-byte elements (sizes already
-// checked to keep the product below 2^62).
-uint64_t tensor_bytes(int64_t B, int64_t H, int64_t N, int64_t d) {
-  return static_cast<uint64_t>(B) * H * N * d * 2u;
-}
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 Range range_of(const void* p, uint64_t bytes) {
   uintptr_t a = reinterpret_cast<uintptr_t>(p);
@@ -35,24 +31,32 @@ Range range_of(const void* p, uint64_t bytes) {
 
 }  // namespace
 
-attn_status check_sizes(int dt, int64_t B, int64_t H, int64_t N, int64_t d) {
+attn_status check_geometry(int dt, const Geometry& g) {
   if (dt != ATTN_F16 && dt != ATTN_BF16) return ATTN_E_UNSUPPORTED;
-  if (d != 64 && d != 128) return ATTN_E_UNSUPPORTED;
-  if (B < 1 || H < 1 || N < 1) return ATTN_E_SHAPE;
+  if (g.d != 64 && g.d != 128) return ATTN_E_UNSUPPORTED;
+  if (g.outer < 1 || g.H < 1 || g.H_kv < 1 || g.rows < 1 || g.max_len < 1) return ATTN_E_SHAPE;
   // Kernels index heads, rows and workgroups with 32-bit integers and
   // element offsets with 64-bit ones.
-  if (B > kMaxI32 || H > kMaxI32 || N > kMaxI32) return ATTN_E_SHAPE;
-  if (B * H > kMaxI32) return ATTN_E_SHAPE;
+  if (g.outer > kMaxI32 || g.H > kMaxI32 || g.rows > kMaxI32) return ATTN_E_SHAPE;
+  // Query heads share key/value heads in equal groups.
+  if (g.H_kv > g.H || g.H % g.H_kv != 0) return ATTN_E_SHAPE;
+  if (g.max_len > g.rows) return ATTN_E_SHAPE;
+  if (g.outer * g.H > kMaxI32) return ATTN_E_SHAPE;
   // One head's rows are addressed through 32-bit buffer offsets.
-  if (N * d * 2 > kMaxI32) return ATTN_E_SHAPE;
-  const int64_t BH = B * H;
-  if (BH > (int64_t(1) << 62) / (N * d * 4)) return ATTN_E_SHAPE;
+  if (g.rows * g.d * 2 > kMaxI32) return ATTN_E_SHAPE;
+  const int64_t heads = g.packed ? g.H : g.outer * g.H;
+  if (heads > (int64_t(1) << 62) / (g.rows * g.d * 4)) return ATTN_E_SHAPE;
   // Grids: one workgroup per (head, 64-row block) at most, and at most 2^32
-  // threads per launch; the widest launch (the backward's row dots) uses d/8
-  // threads per row.
-  if (BH * ceil_div(N, 64) > kMaxI32) return ATTN_E_SHAPE;
-  if (BH * N > (int64_t(1) << 32) / (d / 8) - 256) return ATTN_E_SHAPE;
+  // threads per launch (bounded as if every launch used d/8 threads per row
+  // of the longest sequence).
+  const int64_t nh = g.n_heads();
+  if (nh * ceil_div(g.max_len, 64) > kMaxI32) return ATTN_E_SHAPE;
+  if (nh * g.max_len > (int64_t(1) << 32) / (g.d / 8) - 256) return ATTN_E_SHAPE;
   return ATTN_OK;
+}
+
+attn_status check_sizes(int dt, int64_t B, int64_t H, int64_t N, int64_t d) {
+  return check_geometry(dt, fixed_geometry(B, H, H, N, d));
 }
 
 attn_status check_mask(int mode, int64_t wl, int64_t wr) {
@@ -63,7 +67,7 @@ attn_status check_mask(int mode, int64_t wl, int64_t wr) {
 }
 
 attn_status check_common(const TensorArgs& a) {
-  attn_status s = check_sizes(a.dt, a.B, a.H, a.N, a.d);
+  attn_status s = check_geometry(a.dt, a.g);
   if (s != ATTN_OK) return s;
   for (int i = 0; i < a.n_in; ++i)
     if (a.in[i] == nullptr) return ATTN_E_NULLPTR;
@@ -73,7 +77,7 @@ attn_status check_common(const TensorArgs& a) {
   if (s != ATTN_OK) return s;
   if (!std::isfinite(a.scale)) return ATTN_E_SCALE;
   for (int i = 0; i < a.n_in; ++i)
-    if (!aligned16(a.in[i])) return ATTN_E_ALIGN;
+    if (a.in_align[i] == 4 ? !aligned4(a.in[i]) : !aligned16(a.in[i])) return ATTN_E_ALIGN;
   for (int i = 0; i < a.n_out; ++i)
     if (!aligned16(a.out[i])) return ATTN_E_ALIGN;
   Range in_r[8], out_r[8];
@@ -94,49 +98,95 @@ uint64_t workspace_bytes(int64_t B, int64_t H, int64_t N) {
   return 2u * row_array_bytes(B, H, N);
 }
 
+namespace {
+
+// Tensor sizes of a call: query side, key/value side, per-row float32.
+struct Sizes {
+  uint64_t q, kv, rows;
+};
+
+Sizes sizes_of(const Geometry& g) {
+  return Sizes{static_cast<uint64_t>(g.q_rows()) * g.d * 2u,
+               static_cast<uint64_t>(g.kv_rows()) * g.d * 2u,
+               static_cast<uint64_t>(g.q_rows()) * 4u};
+}
+
+TensorArgs base_args(int dt, const Geometry& g, float scale, int mode, int64_t wl, int64_t wr) {
+  TensorArgs a{};
+  a.dt = dt; a.g = g; a.scale = scale;
+  a.mode = mode; a.wl = wl; a.wr = wr;
+  for (int i = 0; i < 8; ++i) a.in_align[i] = 16;
+  return a;
+}
+
+// The packed batch's row offsets join the inputs (int32, 4-byte aligned).
+void add_offsets(TensorArgs& a, const int32_t* cu_seqlens) {
+  if (!a.g.packed) return;
+  a.in[a.n_in] = cu_seqlens;
+  a.in_bytes[a.n_in] = static_cast<uint64_t>(a.g.outer + 1) * 4u;
+  a.in_align[a.n_in] = 4;
+  ++a.n_in;
+}
+
+}  // namespace
+
+attn_status fwd_check_g(int dt, const void* Q, const void* K, const void* V, const void* O,
+                        const float* lse, const int32_t* cu_seqlens, const Geometry& g,
+                        float scale, int mode, int64_t wl, int64_t wr) {
+  attn_status s = check_geometry(dt, g);
+  if (s != ATTN_OK) return s;
+  const Sizes z = sizes_of(g);
+  TensorArgs a = base_args(dt, g, scale, mode, wl, wr);
+  a.n_in = 3;
+  a.in[0] = Q; a.in[1] = K; a.in[2] = V;
+  a.in_bytes[0] = z.q; a.in_bytes[1] = a.in_bytes[2] = z.kv;
+  add_offsets(a, cu_seqlens);
+  a.n_out = 2;
+  a.out[0] = O; a.out[1] = lse;
+  a.out_bytes[0] = z.q; a.out_bytes[1] = z.rows;
+  return check_common(a);
+}
+
+attn_status bwd_check_g(int dt, const void* Q, const void* K, const void* V, const void* O,
+                        const float* lse, const void* dO, const void* dQ, const void* dK,
+                        const void* dV, const void* ws, size_t ws_bytes,
+                        const int32_t* cu_seqlens, const Geometry& g, float scale, int mode,
+                        int64_t wl, int64_t wr) {
+  attn_status s = check_geometry(dt, g);
+  if (s != ATTN_OK) return s;
+  const Sizes z = sizes_of(g);
+  const uint64_t wb = 2u * row_array_bytes(1, 1, g.q_rows());
+  TensorArgs a = base_args(dt, g, scale, mode, wl, wr);
+  a.n_in = 6;
+  a.in[0] = Q; a.in[1] = K; a.in[2] = V; a.in[3] = O; a.in[4] = lse; a.in[5] = dO;
+  a.in_bytes[0] = a.in_bytes[3] = a.in_bytes[5] = z.q;
+  a.in_bytes[1] = a.in_bytes[2] = z.kv;
+  a.in_bytes[4] = z.rows;
+  add_offsets(a, cu_seqlens);
+  a.n_out = 4;
+  a.out[0] = dQ; a.out[1] = dK; a.out[2] = dV; a.out[3] = ws;
+  a.out_bytes[0] = z.q;
+  a.out_bytes[1] = a.out_bytes[2] = z.kv;
+  a.out_bytes[3] = wb;
+  s = check_common(a);
+  if (s != ATTN_OK) return s;
+  if (ws_bytes < wb) return ATTN_E_WORKSPACE;
+  return ATTN_OK;
+}
+
 attn_status fwd_check(int dt, const void* Q, const void* K, const void* V, const void* O,
                       const float* lse, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
                       int mode, int64_t wl, int64_t wr) {
-  attn_status s = check_sizes(dt, B, H, N, d);
-  if (s != ATTN_OK) return s;
-  const uint64_t tb = tensor_bytes(B, H, N, d);
-  const uint64_t lb = static_cast<uint64_t>(B) * H * N * 4u;
-  TensorArgs a{};
-  a.dt = dt; a.B = B; a.H = H; a.N = N; a.d = d; a.scale = scale;
-  a.mode = mode; a.wl = wl; a.wr = wr;
-  a.n_in = 3;
-  a.in[0] = Q; a.in[1] = K; a.in[2] = V;
-  a.in_bytes[0] = a.in_bytes[1] = a.in_bytes[2] = tb;
-  a.n_out = 2;
-  a.out[0] = O; a.out[1] = lse;
-  a.out_bytes[0] = tb; a.out_bytes[1] = lb;
-  return check_common(a);
+  return fwd_check_g(dt, Q, K, V, O, lse, nullptr, fixed_geometry(B, H, H, N, d), scale, mode, wl,
+                     wr);
 }
 
 attn_status bwd_check(int dt, const void* Q, const void* K, const void* V, const void* O,
                       const float* lse, const void* dO, const void* dQ, const void* dK,
                       const void* dV, const void* ws, size_t ws_bytes, int64_t B, int64_t H,
                       int64_t N, int64_t d, float scale, int mode, int64_t wl, int64_t wr) {
-  attn_status s = check_sizes(dt, B, H, N, d);
-  if (s != ATTN_OK) return s;
-  const uint64_t tb = tensor_bytes(B, H, N, d);
-  const uint64_t lb = static_cast<uint64_t>(B) * H * N * 4u;
-  const uint64_t wb = workspace_bytes(B, H, N);
-  TensorArgs a{};
-  a.dt = dt; a.B = B; a.H = H; a.N = N; a.d = d; a.scale = scale;
-  a.mode = mode; a.wl = wl; a.wr = wr;
-  a.n_in = 6;
-  a.in[0] = Q; a.in[1] = K; a.in[2] = V; a.in[3] = O; a.in[4] = lse; a.in[5] = dO;
-  for (int i = 0; i < 6; ++i) a.in_bytes[i] = tb;
-  a.in_bytes[4] = lb;
-  a.n_out = 4;
-  a.out[0] = dQ; a.out[1] = dK; a.out[2] = dV; a.out[3] = ws;
-  a.out_bytes[0] = a.out_bytes[1] = a.out_bytes[2] = tb;
-  a.out_bytes[3] = wb;
-  s = check_common(a);
-  if (s != ATTN_OK) return s;
-  if (ws_bytes < wb) return ATTN_E_WORKSPACE;
-  return ATTN_OK;
+  return bwd_check_g(dt, Q, K, V, O, lse, dO, dQ, dK, dV, ws, ws_bytes, nullptr,
+                     fixed_geometry(B, H, H, N, d), scale, mode, wl, wr);
 }
 
 }  // namespace attn

@@ -8,20 +8,41 @@
 
 namespace attn {
 
+// The tensors of one call.  Fixed-length batch: Q, O, dO, dQ are
+// [B, H, N, d], K, V, dK, dV are [B, H_kv, N, d], lse is [B, H, N]
+// (outer = B, rows = max_len = N).  Packed variable-length batch: Q, O, dO,
+// dQ are [H, T, d], K, V, dK, dV are [H_kv, T, d], lse is [H, T]
+// (outer = n_seqs, rows = T, max_len = the longest sequence).
+struct Geometry {
+  int64_t outer, H, H_kv, rows, max_len, d;
+  bool packed;
+  int64_t n_heads() const { return outer * H; }       // query heads of a launch
+  int64_t n_kv_heads() const { return outer * H_kv; }
+  // Rows of the query side (lse, workspace arrays) and element counts.
+  int64_t q_rows() const { return packed ? H * rows : outer * H * rows; }
+  int64_t kv_rows() const { return packed ? H_kv * rows : outer * H_kv * rows; }
+};
+
+inline Geometry fixed_geometry(int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d) {
+  return Geometry{B, H, H_kv, N, N, d, false};
+}
+
 struct TensorArgs {
   int dt;
-  int64_t B, H, N, d;
+  Geometry g;
   float scale;
   int mode;
   int64_t wl, wr;
   int n_in, n_out;
   const void* in[8];
   uint64_t in_bytes[8];
+  unsigned in_align[8];  // required alignment of each input (16 unless set)
   const void* out[8];
   uint64_t out_bytes[8];
 };
 
 attn_status check_sizes(int dt, int64_t B, int64_t H, int64_t N, int64_t d);
+attn_status check_geometry(int dt, const Geometry& g);
 attn_status check_mask(int mode, int64_t wl, int64_t wr);
 attn_status check_common(const TensorArgs& a);
 // Bytes of one float32 value per row, padded to 256.
@@ -30,6 +51,17 @@ inline uint64_t row_array_bytes(int64_t B, int64_t H, int64_t N) {
   return (rows * 4u + 255u) / 256u * 256u;
 }
 uint64_t workspace_bytes(int64_t B, int64_t H, int64_t N);
+
+// Validation of a forward / backward call on any geometry (cu_seqlens is
+// read only for a packed batch).
+attn_status fwd_check_g(int dt, const void* Q, const void* K, const void* V, const void* O,
+                        const float* lse, const int32_t* cu_seqlens, const Geometry& g,
+                        float scale, int mode, int64_t wl, int64_t wr);
+attn_status bwd_check_g(int dt, const void* Q, const void* K, const void* V, const void* O,
+                        const float* lse, const void* dO, const void* dQ, const void* dK,
+                        const void* dV, const void* ws, size_t ws_bytes,
+                        const int32_t* cu_seqlens, const Geometry& g, float scale, int mode,
+                        int64_t wl, int64_t wr);
 
 attn_status fwd_check(int dt, const void* Q, const void* K, const void* V, const void* O,
                       const float* lse, int64_t B, int64_t H, int64_t N, int64_t d, float scale,

@@ -78,7 +78,8 @@ typedef enum attn_mask_mode {
 typedef enum attn_status {
   ATTN_OK = 0,
   ATTN_E_NULLPTR = 1,     /* a required pointer is NULL */
-  ATTN_E_SHAPE = 2,       /* B, H or N < 1, or sizes too large to index */
+  ATTN_E_SHAPE = 2,       /* B, H or N < 1, sizes too large to index, H not a multiple
+                             of H_kv, or max_seqlen outside [1, T] */
   ATTN_E_UNSUPPORTED = 3, /* dtype or head size d not supported */
   ATTN_E_MASK = 4,        /* unknown mask mode or negative window */
   ATTN_E_SCALE = 5,       /* scale is NaN or infinite */
@@ -135,6 +136,72 @@ attn_status attn_bwd(attn_dtype dt, const void* Q, const void* K, const void* V,
                      void* workspace, size_t workspace_bytes, int64_t B, int64_t H, int64_t N,
                      int64_t d, float scale, attn_mask_mode mode, int64_t window_left,
                      int64_t window_right, void* stream);
+
+/*
+ * Grouped-query and variable-length variants (P1 §5 names both among
+ * FlashAttention's extensions; the pages give no formulas, so the readings
+ * below are this library's).
+ *
+ * Grouped-query attention (GQA; multi-query attention is H_kv = 1): the H
+ * query heads share H_kv key/value heads, H a multiple of H_kv, and query
+ * head h reads key/value head h / (H / H_kv) -- consecutive query heads
+ * share one.  With H_kv = H these calls equal attn_fwd / attn_bwd.
+ *
+ * Packed variable-length batch: n_seqs sequences are stored one after the
+ * other along the row axis, T rows in all: Q, O (and dO, dQ) are [H, T, d],
+ * K, V (and dK, dV) are [H_kv, T, d], lse is [H, T]; sequence s occupies
+ * rows [cu_seqlens[s], cu_seqlens[s+1]).  Each sequence attends only to
+ * itself, and the mask applies to positions counted from the sequence's
+ * first row (causal: key j <= query i within the sequence).
+ *   cu_seqlens  in: int32 device array of n_seqs + 1 row offsets, 4-byte
+ *               aligned, caller-owned.  The caller guarantees
+ *               0 = cu[0] <= cu[1] <= ... <= cu[n_seqs] <= T and
+ *               cu[s+1] - cu[s] <= max_seqlen.  These values live on the
+ *               device and are not validated; the kernels clamp every
+ *               sequence to rows [0, T), so malformed offsets never make
+ *               them access memory outside the tensors, but the results for
+ *               such offsets are unspecified.  Rows outside every sequence
+ *               are not written.  Empty sequences are allowed.
+ *   n_seqs      >= 1;  max_seqlen in [1, T];  total = T >= 1.
+ * The size rules of the conventions apply with B*H*N replaced by
+ * n_seqs*H*max_seqlen for the thread bound and by H*T for the tensor sizes.
+ * The backward's workspace is attn_bwd_workspace_bytes(dt, 1, H, T, d)
+ * (two float32 values per query-side row, as for attn_bwd).
+ */
+
+/* attn_fwd_gqa -- attn_fwd with K, V of shape [B, H_kv, N, d]. */
+attn_status attn_fwd_gqa(attn_dtype dt, const void* Q, const void* K, const void* V, void* O,
+                         float* lse, int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d,
+                         float scale, attn_mask_mode mode, int64_t window_left,
+                         int64_t window_right, void* stream);
+
+/*
+ * attn_bwd_gqa -- attn_bwd with K, V, dK, dV of shape [B, H_kv, N, d]:
+ * dK and dV of a key/value head sum the contributions of all the query
+ * heads that read it (deterministic, no atomics).  Workspace:
+ * attn_bwd_workspace_bytes(dt, B, H, N, d).
+ */
+attn_status attn_bwd_gqa(attn_dtype dt, const void* Q, const void* K, const void* V,
+                         const void* O, const float* lse, const void* dO, void* dQ, void* dK,
+                         void* dV, void* workspace, size_t workspace_bytes, int64_t B, int64_t H,
+                         int64_t H_kv, int64_t N, int64_t d, float scale, attn_mask_mode mode,
+                         int64_t window_left, int64_t window_right, void* stream);
+
+/* attn_fwd_varlen -- forward over a packed variable-length batch (see above). */
+attn_status attn_fwd_varlen(attn_dtype dt, const void* Q, const void* K, const void* V, void* O,
+                            float* lse, const int32_t* cu_seqlens, int64_t n_seqs,
+                            int64_t max_seqlen, int64_t total, int64_t H, int64_t H_kv,
+                            int64_t d, float scale, attn_mask_mode mode, int64_t window_left,
+                            int64_t window_right, void* stream);
+
+/* attn_bwd_varlen -- backward over a packed variable-length batch (see above). */
+attn_status attn_bwd_varlen(attn_dtype dt, const void* Q, const void* K, const void* V,
+                            const void* O, const float* lse, const void* dO, void* dQ, void* dK,
+                            void* dV, void* workspace, size_t workspace_bytes,
+                            const int32_t* cu_seqlens, int64_t n_seqs, int64_t max_seqlen,
+                            int64_t total, int64_t H, int64_t H_kv, int64_t d, float scale,
+                            attn_mask_mode mode, int64_t window_left, int64_t window_right,
+                            void* stream);
 
 /* attn_status_str -- static, NUL-terminated description of a status code. */
 const char* attn_status_str(attn_status s);

@@ -8,13 +8,19 @@
 //   * kv_tile_range / q_tile_range visit exactly the tiles holding at least
 //     one allowed pair (the allowed tiles of a block form one interval);
 //   * tile_all_allowed / tile_none_allowed agree with the enumeration;
-//   * xcd_remap is a bijection and gives each die a contiguous run.
+//   * xcd_remap is a bijection and gives each die a contiguous run;
+//   * query_head_rows / kv_head_rows map grouped-query heads to their
+//     key/value heads (query head h of a batch entry or sequence reads
+//     key/value head h / group) and packed sequences to their rows, and keep
+//     every head inside its tensor whatever row offsets they are given.
+#include <cstdint>
 #include <cstdio>
 #include <cstdlib>
 #include <vector>
 
 #include "attn.h"
 #include "plan.hpp"
+#include "validate.hpp"
 
 using namespace attn;
 
@@ -134,8 +140,70 @@ int main() {
     }
     for (int64_t i = 0; i < n; ++i) CHECK(seen[i] == 1, "remap not a bijection n=%lld", (long long)n);
   }
+  // Head mapping, fixed-length batches: B x H query heads over B x H_kv
+  // key/value heads, every row of a head.
+  for (int64_t H = 1; H <= 12; ++H) {
+    for (int64_t H_kv = 1; H_kv <= H; ++H_kv) {
+      if (H % H_kv) continue;
+      const int64_t group = H / H_kv, B = 3, rows = 5;
+      for (int64_t b = 0; b < B; ++b)
+        for (int64_t h = 0; h < H; ++h) {
+          const HeadRows r = query_head_rows(b * H + h, H, group, rows, false, 0, 0);
+          CHECK(r.q_row0 == (b * H + h) * rows && r.len == rows, "fixed q rows H=%lld", (long long)H);
+          CHECK(r.kv_row0 == (b * H_kv + h / group) * rows, "fixed kv head H=%lld H_kv=%lld",
+                (long long)H, (long long)H_kv);
+        }
+      for (int64_t y = 0; y < B * H_kv; ++y) {
+        const KvHeadRows k = kv_head_rows(y, H_kv, group, rows, false, 0, 0);
+        CHECK(k.kv_row0 == y * rows && k.len == rows, "fixed kv rows");
+        for (int64_t g = 0; g < group; ++g) {
+          // member g of the group is the query head that reads this key/value head
+          const int64_t x = (y / H_kv) * H + (y % H_kv) * group + g;
+          const HeadRows r = query_head_rows(x, H, group, rows, false, 0, 0);
+          CHECK(r.kv_row0 == k.kv_row0 && r.q_row0 == k.q_row0 + g * k.q_stride, "fixed group");
+        }
+      }
+    }
+  }
+  // Packed batches: sequence offsets, including malformed ones, stay inside
+  // the head's T rows.
+  {
+    const int64_t T = 20;
+    const int64_t offs[][2] = {{0, 20}, {0, 0}, {3, 9}, {19, 20}, {-5, 4}, {7, 3},
+                               {15, 40}, {25, 30}, {-9, -2}, {20, 20}};
+    for (auto& o : offs) {
+      for (int64_t H = 1; H <= 6; ++H)
+        for (int64_t H_kv = 1; H_kv <= H; ++H_kv) {
+          if (H % H_kv) continue;
+          const int64_t group = H / H_kv, n_seqs = 2;
+          for (int64_t x = 0; x < n_seqs * H; ++x) {
+            const HeadRows r = query_head_rows(x, H, group, T, true, o[0], o[1]);
+            const int64_t h = x % H;
+            CHECK(r.len >= 0 && r.q_row0 >= h * T && r.q_row0 + r.len <= (h + 1) * T,
+                  "packed q rows inside head");
+            CHECK(r.kv_row0 >= (h / group) * T && r.kv_row0 + r.len <= (h / group + 1) * T,
+                  "packed kv rows inside head");
+            CHECK(r.q_row0 - h * T == r.kv_row0 - (h / group) * T, "same sequence rows");
+            if (o[0] >= 0 && o[0] <= o[1] && o[1] <= T)
+              CHECK(r.q_row0 == h * T + o[0] && r.len == o[1] - o[0], "well-formed offsets");
+          }
+          for (int64_t y = 0; y < n_seqs * H_kv; ++y) {
+            const KvHeadRows k = kv_head_rows(y, H_kv, group, T, true, o[0], o[1]);
+            const int64_t kvh = y % H_kv;
+            CHECK(k.len >= 0 && k.kv_row0 >= kvh * T && k.kv_row0 + k.len <= (kvh + 1) * T,
+                  "packed kv-major rows inside head");
+            for (int64_t g = 0; g < group; ++g) {
+              const int64_t h = kvh * group + g;
+              const HeadRows r = query_head_rows((y / H_kv) * H + h, H, group, T, true, o[0], o[1]);
+              CHECK(r.q_row0 == k.q_row0 + g * k.q_stride && r.kv_row0 == k.kv_row0 &&
+                        r.len == k.len, "packed group member");
+            }
+          }
+        }
+    }
+  }
   // Validation: null, sizes, masks, scale, alignment, aliasing.
-  char* base = static_cast<char*>(std::aligned_alloc(256, 1 << 16));
+  char* base = static_cast<char*>(std::aligned_alloc(256, 1 << 17));
   const void *Q = base, *K = base + 4096, *V = base + 8192;
   void* O = base + 12288;
   float* L = reinterpret_cast<float*>(base + 16384);
@@ -169,6 +237,37 @@ int main() {
   CHECK(attn_bwd_check(ATTN_F16, Q, K, V, O, L, O, dQ, dK, dV, nullptr, ws, B, H, N, d, 0.1f, ATTN_MASK_CAUSAL, 0, 0) == ATTN_E_NULLPTR, "bwd ws null");
   CHECK(attn_bwd_check(ATTN_F16, Q, K, V, O, L, O, dQ, dQ, dV, W, ws, B, H, N, d, 0.1f, ATTN_MASK_CAUSAL, 0, 0) == ATTN_E_ALIAS, "bwd alias");
   CHECK(attn_bwd_check(ATTN_F16, Q, K, V, O, L, O, dQ, dK, dV, const_cast<void*>(Q), ws, B, H, N, d, 0.1f, ATTN_MASK_CAUSAL, 0, 0) == ATTN_E_ALIAS, "bwd ws alias");
+  // Grouped-query and packed geometries (the validation every entry point runs).
+  {
+    // Fixed-length GQA: B = 1, H = 4, H_kv = 2, N = 8, d = 64: Q/O 4 KiB, K/V 2 KiB.
+    const Geometry g = fixed_geometry(1, 4, 2, 8, 64);
+    char* q = base + 4096 * 8;
+    const void *gk = q + 4096, *gv = q + 6144;
+    void* go = q + 8192;
+    float* gl = reinterpret_cast<float*>(q + 12288);
+    CHECK(fwd_check_g(ATTN_F16, q, gk, gv, go, gl, nullptr, g, 0.1f, 0, 0, 0) == ATTN_OK, "gqa ok");
+    CHECK(fwd_check_g(ATTN_F16, q, gk, gv, q + 6144 + 1024, gl, nullptr, g, 0.1f, 0, 0, 0) == ATTN_E_ALIAS, "gqa V sized by H_kv");
+    CHECK(fwd_check_g(ATTN_F16, q, gk, gv, q + 6144 + 2048, gl, nullptr, g, 0.1f, 0, 0, 0) == ATTN_OK, "gqa V ends where O starts");
+    CHECK(fwd_check_g(ATTN_F16, q, gk, gv, go, gl, nullptr, fixed_geometry(1, 6, 4, 8, 64), 0.1f, 0, 0, 0) == ATTN_E_SHAPE, "H not a multiple of H_kv");
+    CHECK(fwd_check_g(ATTN_F16, q, gk, gv, go, gl, nullptr, fixed_geometry(1, 2, 4, 8, 64), 0.1f, 0, 0, 0) == ATTN_E_SHAPE, "H_kv > H");
+    CHECK(fwd_check_g(ATTN_F16, q, gk, gv, go, gl, nullptr, fixed_geometry(1, 4, 0, 8, 64), 0.1f, 0, 0, 0) == ATTN_E_SHAPE, "H_kv 0");
+    // Packed: n_seqs = 3, T = 8, max_len 5, H = 4, H_kv = 1.
+    const Geometry pg{3, 4, 1, 8, 5, 64, true};
+    const int32_t* cu = reinterpret_cast<const int32_t*>(q + 16384);
+    CHECK(fwd_check_g(ATTN_F16, q, gk, gv, go, gl, cu, pg, 0.1f, 1, 0, 0) == ATTN_OK, "packed ok");
+    CHECK(fwd_check_g(ATTN_F16, q, gk, gv, go, gl, nullptr, pg, 0.1f, 1, 0, 0) == ATTN_E_NULLPTR, "packed cu null");
+    CHECK(fwd_check_g(ATTN_F16, q, gk, gv, go, gl, reinterpret_cast<const int32_t*>(q + 16386), pg, 0.1f, 1, 0, 0) == ATTN_E_ALIGN, "packed cu align");
+    CHECK(fwd_check_g(ATTN_F16, q, gk, gv, go, gl, reinterpret_cast<const int32_t*>(q + 16388), pg, 0.1f, 1, 0, 0) == ATTN_OK, "packed cu 4-byte aligned");
+    CHECK(fwd_check_g(ATTN_F16, q, gk, gv, go, gl, reinterpret_cast<const int32_t*>(q + 12288), pg, 0.1f, 1, 0, 0) == ATTN_E_ALIAS, "packed cu under lse");
+    CHECK(fwd_check_g(ATTN_F16, q, gk, gv, go, gl, cu, Geometry{3, 4, 1, 8, 9, 64, true}, 0.1f, 1, 0, 0) == ATTN_E_SHAPE, "max_len > T");
+    CHECK(fwd_check_g(ATTN_F16, q, gk, gv, go, gl, cu, Geometry{0, 4, 1, 8, 5, 64, true}, 0.1f, 1, 0, 0) == ATTN_E_SHAPE, "no sequences");
+    const size_t pws = attn_bwd_workspace_bytes(ATTN_F16, 1, 4, 8, 64);
+    void* W2 = q + 20480;
+    CHECK(bwd_check_g(ATTN_F16, q, gk, gv, go, gl, go, q + 24576, q + 28672, q + 30720, W2, pws, cu, pg, 0.1f, 1, 0, 0) == ATTN_OK, "packed bwd ok");
+    CHECK(bwd_check_g(ATTN_F16, q, gk, gv, go, gl, go, q + 24576, q + 28672, q + 30720, W2, pws - 4, cu, pg, 0.1f, 1, 0, 0) == ATTN_E_WORKSPACE, "packed bwd ws");
+    CHECK(bwd_check_g(ATTN_F16, q, gk, gv, go, gl, go, q + 24576, q + 28672, q + 28672 + 512, W2, pws, cu, pg, 0.1f, 1, 0, 0) == ATTN_E_ALIAS, "packed dK/dV overlap");
+    CHECK(bwd_check_g(ATTN_F16, q, gk, gv, go, gl, go, q + 24576, q + 28672, q + 28672 + 1024, W2, pws, cu, pg, 0.1f, 1, 0, 0) == ATTN_OK, "packed dK/dV sized by H_kv");
+  }
   for (int s = 0; s <= 9; ++s) CHECK(attn_status_str(static_cast<attn_status>(s)) != nullptr, "str");
   std::free(base);
   std::printf("plan_check: %d failures\n", failures);

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 14, names
     lib = ea.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -59,6 +59,58 @@ def test_launching_entry_points_reject_bad_arguments_before_any_hip_call():
     assert lib.attn_bwd(*args) == 8
     # nothing was written: the buffer is still zero
     assert bytes(buf) == b"\0" * len(buf)
+
+
+def test_grouped_and_packed_entry_points_reject_bad_arguments_before_any_hip_call():
+    lib = ea.lib()
+    buf = ctypes.create_string_buffer(1 << 16)
+    base = (ctypes.addressof(buf) + 255) // 256 * 256
+    Q, K, V, O, L = base, base + 4096, base + 8192, base + 12288, base + 16384
+    cu = base + 20480
+    # H not a multiple of H_kv, H_kv larger than H, H_kv zero
+    assert lib.attn_fwd_gqa(1, Q, K, V, O, L, 1, 6, 4, 8, 64, 0.1, 0, 0, 0, None) == 2
+    assert lib.attn_fwd_gqa(1, Q, K, V, O, L, 1, 2, 4, 8, 64, 0.1, 0, 0, 0, None) == 2
+    assert lib.attn_fwd_gqa(1, Q, K, V, O, L, 1, 2, 0, 8, 64, 0.1, 0, 0, 0, None) == 2
+    # O overlapping V, which has H_kv = 1 head (1 KiB at N = 8, d = 64)
+    assert lib.attn_fwd_gqa(1, Q, K, V, V + 512, L, 1, 4, 1, 8, 64, 0.1, 0, 0, 0, None) == 7
+    # packed: NULL offsets, misaligned offsets, max_seqlen > T, no sequences,
+    # offsets overlapping an output, unsupported d
+    vargs = lambda cu_, n, mx, T, d=64: [0, Q, K, V, O, L, cu_, n, mx, T, 2, 1, d, 0.1, 1, 0, 0,
+                                         None]
+    assert lib.attn_fwd_varlen(*vargs(None, 2, 4, 8)) == 1
+    assert lib.attn_fwd_varlen(*vargs(cu + 2, 2, 4, 8)) == 6
+    assert lib.attn_fwd_varlen(*vargs(cu, 2, 9, 8)) == 2
+    assert lib.attn_fwd_varlen(*vargs(cu, 0, 4, 8)) == 2
+    assert lib.attn_fwd_varlen(*vargs(L, 2, 4, 8)) == 7
+    assert lib.attn_fwd_varlen(*vargs(cu, 2, 4, 8, 96)) == 3
+    # backward: workspace below attn_bwd_workspace_bytes(dt, 1, H, T, d)
+    ws = ea.attn_bwd_workspace_bytes(__import__("torch").float16, 1, 2, 8, 64)
+    b = [0, Q, K, V, O, L, O, base + 24576, base + 28672, base + 32768, base + 36864, ws - 4,
+         cu, 2, 4, 8, 2, 1, 64, 0.1, 1, 0, 0, None]
+    assert lib.attn_bwd_varlen(*b) == 8
+    g = [0, Q, K, V, O, L, O, base + 24576, base + 28672, base + 32768, base + 36864, ws,
+         1, 6, 4, 8, 64, 0.1, 1, 0, 0, None]
+    assert lib.attn_bwd_gqa(*g) == 2
+    assert bytes(buf) == b"\0" * len(buf)
+
+
+def test_binding_rejects_mismatched_grouped_and_packed_shapes():
+    """Shape checks of the wrappers (CPU tensors: they raise before any GPU use)."""
+    import torch
+    q = torch.zeros(1, 4, 8, 64, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        ea.attn_fwd(q, torch.zeros(1, 2, 9, 64, dtype=torch.float16),
+                    torch.zeros(1, 2, 9, 64, dtype=torch.float16))
+    with pytest.raises(ValueError):
+        ea.attn_fwd(q, torch.zeros(1, 2, 8, 64, dtype=torch.float16),
+                    torch.zeros(1, 1, 8, 64, dtype=torch.float16))
+    qp = torch.zeros(4, 8, 64, dtype=torch.float16)
+    kp = torch.zeros(2, 8, 64, dtype=torch.float16)
+    cu = torch.tensor([0, 3, 8], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        ea.attn_fwd_varlen(qp, torch.zeros(2, 7, 64, dtype=torch.float16), kp, cu, 5)
+    with pytest.raises(ValueError):
+        ea.attn_fwd_varlen(qp, kp, kp, cu, 5)  # inputs on the CPU
 
 
 def test_fwd_tiles():

@@ -15,6 +15,11 @@ Recipe (the same for every workload):
     (b, h), b-major then h, uniformly without replacement from the same
     generator, and multiplies those K rows by 8 (a power of two, so exact).
 
+Grouped-query inputs draw K and V with H_kv heads; packed variable-length inputs
+are [H, T, d] (K, V [H_kv, T, d]) with row offsets from ``packed_offsets`` and
+lengths, for the mixed-length workloads, from ``length_mix`` (log-uniform,
+seeded).
+
 The pages measure on model-shaped random activations (LLaMA-7B / LLaMA-13B
 attention shapes, and a long-sequence window case); i.i.d. N(0, 1) inputs of the
 same shapes stand in for them.
@@ -100,6 +105,44 @@ def draw(B: int, H: int, N: int, d: int, dtype: str, seed: int, *, with_do: bool
                 idx = torch.from_numpy(rows[b, h])
                 kk[b, h, idx] = kk[b, h, idx] * mul
         out["outlier_rows"] = rows
+    return out
+
+
+def draw_grouped(B: int, H: int, H_kv: int, N: int, d: int, dtype: str, seed: int, *,
+                 with_do: bool = False) -> dict:
+    """Q [B, H, N, d], K and V [B, H_kv, N, d] (and dO [B, H, N, d]), in that order."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for key, heads in (("q", H), ("k", H_kv), ("v", H_kv)) + ((("do", H),) if with_do else ()):
+        out[key] = _round(rng.standard_normal((B, heads, N, d), dtype=np.float32), dtype)
+    return out
+
+
+def draw_packed(H: int, H_kv: int, T: int, d: int, dtype: str, seed: int, *,
+                with_do: bool = False) -> dict:
+    """Packed batch: Q [H, T, d], K and V [H_kv, T, d] (and dO [H, T, d]), in that order."""
+    rng = np.random.default_rng(seed)
+    out = {}
+    for key, heads in (("q", H), ("k", H_kv), ("v", H_kv)) + ((("do", H),) if with_do else ()):
+        out[key] = _round(rng.standard_normal((heads, T, d), dtype=np.float32), dtype)
+    return out
+
+
+def packed_offsets(lengths) -> np.ndarray:
+    """Row offsets (int32, n + 1 entries, starting at 0) of sequences packed in order."""
+    return np.concatenate([[0], np.cumsum(np.asarray(lengths, dtype=np.int64))]).astype(np.int32)
+
+
+def length_mix(total: int, lo: int, hi: int, seed: int) -> list:
+    """Sequence lengths drawn log-uniformly from [lo, hi] until they fill ``total`` rows
+    (the last one is cut to fit): a mixed-length packed batch of exactly ``total`` rows."""
+    rng = np.random.default_rng(seed)
+    out, used = [], 0
+    while used < total:
+        n = int(round(float(np.exp(rng.uniform(np.log(lo), np.log(hi))))))
+        n = min(max(n, 1), total - used)
+        out.append(n)
+        used += n
     return out
 
 
