@@ -2,7 +2,8 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-A step is one attn_fwd call over the whole batch of the workload (host plan,
+A step is one attn_fwd call (attn_fwd_varlen for a packed workload) over the
+whole batch of the workload (host plan,
 Q load, K/V streaming, score products, masking, online softmax, output
 products, epilogue: the whole forward path), with inputs already resident in
 device memory.  The default workload is B=4, H=32, N=4096, d=128, bf16, no
@@ -45,8 +46,13 @@ def allowed_pairs(N: int, mode: str, wl: int, wr: int) -> int:
     return total
 
 
+def pairs_per_head(w) -> int:
+    """Allowed (query, key) pairs of one query head over all its sequences."""
+    return sum(allowed_pairs(n, w.mask, w.window_left, w.window_right) for n in w.lengths)
+
+
 def fwd_flops(w) -> int:
-    return 4 * w.d * w.B * w.H * allowed_pairs(w.N, w.mask, w.window_left, w.window_right)
+    return 4 * w.d * w.H * pairs_per_head(w)
 
 
 def mask_arg(w):
@@ -57,33 +63,53 @@ def mask_arg(w):
     return (w.window_left, w.window_right)
 
 
-def cpu_baseline(w, inp, budget_s: float = 12.0, max_heads: int = 128):
-    """The fp64 oracle as it stands, on whole heads of the workload, until ~budget_s."""
+def oracle_units(w, inp):
+    """(label, q, k, v) float64 arrays of one query head of one sequence each, in order:
+    the head's own Q rows and its key/value head's K, V rows."""
+    from workloads import to_f64
+    g = w.H // w.kv_heads
+    if w.packed:
+        cu = inp["cu_seqlens"].numpy()
+        for s_ in range(len(cu) - 1):
+            lo, hi = int(cu[s_]), int(cu[s_ + 1])
+            for h in range(w.H):
+                yield ((s_, h),) + tuple(to_f64(inp[x][i, lo:hi])
+                                         for x, i in (("q", h), ("k", h // g), ("v", h // g)))
+    else:
+        for b in range(w.B):
+            for h in range(w.H):
+                yield ((b, h),) + tuple(to_f64(inp[x][b, i])
+                                        for x, i in (("q", h), ("k", h // g), ("v", h // g)))
+
+
+def cpu_baseline(w, inp, budget_s: float = 12.0, max_units: int = 128):
+    """The fp64 oracle as it stands, on whole heads (whole sequences of one head for a
+    packed batch) of the workload, until ~budget_s."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     import oracle
-    from workloads import to_f64
 
-    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
-    done = 0
+    done, pairs = 0, 0
     t0 = time.perf_counter()
-    rb = 1024 if w.N > 8192 else w.N
-    while done < min(max_heads, len(heads)):
-        b, h = heads[done]
-        q, k, v = (to_f64(inp[x][b, h]) for x in ("q", "k", "v"))
-        for r0 in range(0, w.N, rb):
-            rows = np.arange(r0, min(w.N, r0 + rb))
+    for _, q, k, v in oracle_units(w, inp):
+        n = q.shape[0]
+        rb = 1024 if n > 8192 else n
+        for r0 in range(0, n, rb):
+            rows = np.arange(r0, min(n, r0 + rb))
             oracle.forward_rows(rows, q, k, v, w.scale, w.mask, w.window_left, w.window_right)
+        pairs += allowed_pairs(n, w.mask, w.window_left, w.window_right)
         done += 1
-        if time.perf_counter() - t0 > budget_s:
+        if done >= max_units or time.perf_counter() - t0 > budget_s:
             break
     dt = time.perf_counter() - t0
-    flops = 4 * w.d * done * allowed_pairs(w.N, w.mask, w.window_left, w.window_right)
+    flops = 4 * w.d * pairs
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    unit = "sequence-heads" if w.packed else "heads"
+    total = w.H * len(w.lengths)
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{done} of {len(heads)} heads, all {w.N} rows each (fp64 numpy, S and P "
+            "sample": f"{done} of {total} {unit}, all their rows (fp64 numpy, S and P "
                       f"materialised per head), {dt:.1f} s"}
 
 
@@ -113,11 +139,17 @@ def main():
     inp = make_inputs(w)
     q, k, v = (inp[x].to("cuda") for x in ("q", "k", "v"))
     o = torch.empty_like(q)
-    lse = torch.empty((w.B, w.H, w.N), dtype=torch.float32, device="cuda")
+    lse = torch.empty(tuple(q.shape[:-1]), dtype=torch.float32, device="cuda")
     mask = mask_arg(w)
+    if w.packed:
+        cu = inp["cu_seqlens"].to("cuda")
+        max_len = max(w.lengths)
 
     def step():
-        ea.attn_fwd(q, k, v, mask=mask, scale=w.scale, out=o, lse=lse)
+        if w.packed:
+            ea.attn_fwd_varlen(q, k, v, cu, max_len, mask=mask, scale=w.scale, out=o, lse=lse)
+        else:
+            ea.attn_fwd(q, k, v, mask=mask, scale=w.scale, out=o, lse=lse)
 
     for _ in range(args.warmup):
         step()
@@ -158,12 +190,16 @@ def main():
                          dtype=torch.uint8, device="cuda")
 
         def bstep():
-            ea.attn_bwd(q, k, v, o, lse, do, mask=mask, scale=w.scale, workspace=ws)
+            if w.packed:
+                ea.attn_bwd_varlen(q, k, v, o, lse, do, cu, max_len, mask=mask, scale=w.scale,
+                                   workspace=ws)
+            else:
+                ea.attn_bwd(q, k, v, o, lse, do, mask=mask, scale=w.scale, workspace=ws)
 
         for _ in range(args.warmup):
             bstep()
         b_wall, b_ms, b_pct = timed(bstep)
-        bflops = 10 * w.d * w.B * w.H * allowed_pairs(w.N, w.mask, w.window_left, w.window_right)
+        bflops = 10 * w.d * w.H * pairs_per_head(w)
         backward = {"ms_per_call": round(b_wall, 5),
                     "kernel_ms": round(b_ms, 5),
                     "kernel_ms_per_call": b_pct,
@@ -193,8 +229,21 @@ def main():
         if tr.get("kernel_source_sha") == kernel_source_sha():
             traffic = round(tr.get("bytes_per_launch"))
 
+    if w is FULL_N4096:
+        metric = "attention fwd TFLOP/s (and % of bf16 MFMA peak) at B4 H32 N4096 d128"
+    else:
+        metric = f"attention fwd TFLOP/s ({w.name})"
+    config = {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "mask": w.mask,
+              "window_left": w.window_left, "window_right": w.window_right,
+              "scale": w.scale, "global_batch": w.B, "seq_len": w.N, "parallelism": "none"}
+    if w.kv_heads != w.H:
+        config["H_kv"] = w.kv_heads
+    if w.packed:
+        config.update({"packed_rows": w.N, "n_seqs": len(w.lengths), "max_seqlen": max(w.lengths),
+                       "lengths": f"log-uniform in [{w.packed_lo}, {w.packed_hi}], "
+                                  f"seed {w.packed_seed}"})
     rec = {
-        "metric": "attention fwd TFLOP/s (and % of bf16 MFMA peak) at B4 H32 N4096 d128",
+        "metric": metric,
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -206,9 +255,7 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded i.i.d. N(0,1) inputs of the workload's shape)",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "mask": w.mask,
-                   "window_left": w.window_left, "window_right": w.window_right,
-                   "scale": w.scale, "global_batch": w.B, "seq_len": w.N, "parallelism": "none"},
+        "config": config,
         "tokens_per_s": round(w.B * w.N / (ms_wall * 1e-3), 1),
         "frac_of_peak": round(value / peak, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,

@@ -197,6 +197,39 @@ ATTN_HD void fwd_work_item(int64_t wg, int64_t n_heads, int64_t n_qblk, int mode
   *qblk = (mode == kCausal) ? (n_qblk - 1 - qb) : qb;
 }
 
+// Work item -> (head x = s * heads + h, block) for a packed variable-length
+// batch of n_seqs sequences with `heads` heads each and n_blk blocks of the
+// longest sequence.  Work per head varies with its sequence's length, so the
+// equal-count runs of xcd_remap would leave the dies unevenly loaded.  With
+// `heads` a multiple of kNumXcd, die x instead takes heads
+// [x * heads/8, (x+1) * heads/8) of every sequence -- every die gets the same
+// share of every sequence, and query heads that read one key/value head stay
+// on one die's L2 -- and runs its items block by block, heaviest first:
+// descending block index (a causal query block's work grows with its index,
+// and without a mask only long sequences have high indices), or ascending
+// when `ascending` (a causal key block's work shrinks with its index).  For
+// other head counts the order is the same block by block, over all heads,
+// dealt round-robin to the dies.
+ATTN_HD void packed_work_item(int64_t wg, int64_t heads, int64_t n_seqs, int64_t n_blk,
+                              bool ascending, int64_t* head, int64_t* blk) {
+  const int64_t per_blk = heads * n_seqs;
+  int64_t b, s, h;
+  if (heads % kNumXcd == 0) {
+    const int64_t hp = heads / kNumXcd, xcd = wg % kNumXcd, slot = wg / kNumXcd;
+    b = slot / (hp * n_seqs);
+    const int64_t rem = slot % (hp * n_seqs);
+    s = rem / hp;
+    h = xcd * hp + rem % hp;
+  } else {
+    b = wg / per_blk;
+    const int64_t rem = wg % per_blk;
+    s = rem / heads;
+    h = rem % heads;
+  }
+  *head = s * heads + h;
+  *blk = ascending ? b : n_blk - 1 - b;
+}
+
 // Work item -> (head, key block) of the backward's key-major pass.  Under a
 // causal mask key block b sees every query tile from b on, so block 0 does
 // up to 16 times the work of the last one at N = 4096: the order is then

@@ -140,6 +140,33 @@ int main() {
     }
     for (int64_t i = 0; i < n; ++i) CHECK(seen[i] == 1, "remap not a bijection n=%lld", (long long)n);
   }
+  // packed_work_item: a bijection onto (head, block); with a head count that
+  // is a multiple of 8 each die gets heads/8 consecutive heads of every
+  // sequence, and every die's items run block by block in the stated order.
+  for (int64_t heads : {1, 2, 3, 8, 16, 24, 40}) {
+    for (int64_t n_seqs : {1, 2, 5}) {
+      for (int64_t n_blk : {1, 3, 7}) {
+        for (int asc = 0; asc < 2; ++asc) {
+          const int64_t n = heads * n_seqs * n_blk;
+          std::vector<int> seen(n, 0);
+          std::vector<int64_t> last_blk(kNumXcd, asc ? -1 : n_blk);
+          for (int64_t w = 0; w < n; ++w) {
+            int64_t x, b;
+            packed_work_item(w, heads, n_seqs, n_blk, asc != 0, &x, &b);
+            CHECK(x >= 0 && x < heads * n_seqs && b >= 0 && b < n_blk, "packed item range");
+            if (x < 0 || x >= heads * n_seqs || b < 0 || b >= n_blk) continue;
+            seen[b * heads * n_seqs + x]++;
+            const int64_t die = w % kNumXcd;
+            if (heads % kNumXcd == 0)
+              CHECK((x % heads) / (heads / kNumXcd) == die, "packed head on its die");
+            CHECK(asc ? b >= last_blk[die] : b <= last_blk[die], "packed block order");
+            last_blk[die] = b;
+          }
+          for (int64_t i = 0; i < n; ++i) CHECK(seen[i] == 1, "packed order not a bijection");
+        }
+      }
+    }
+  }
   // Head mapping, fixed-length batches: B x H query heads over B x H_kv
   // key/value heads, every row of a head.
   for (int64_t H = 1; H <= 12; ++H) {

@@ -50,6 +50,27 @@ class Workload:
     backward: bool = False       # also draw dO (forward + backward workload)
     outlier_frac: float = 0.0    # fraction of K rows per head scaled by outlier_mul
     outlier_mul: float = 1.0
+    H_kv: int = 0                # key/value heads (grouped-query); 0 means H
+    # Packed variable-length batch: N is then the total row count T (B = 1),
+    # split into sequences by length_mix(N, packed_lo, packed_hi, packed_seed).
+    packed_lo: int = 0
+    packed_hi: int = 0
+    packed_seed: int = 0
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H_kv if self.H_kv > 0 else self.H
+
+    @property
+    def packed(self) -> bool:
+        return self.packed_hi > 0
+
+    @property
+    def lengths(self) -> list:
+        """Sequence lengths of a packed workload; [N] * B otherwise."""
+        if not self.packed:
+            return [self.N] * self.B
+        return length_mix(self.N, self.packed_lo, self.packed_hi, self.packed_seed)
 
     @property
     def scale(self) -> float:
@@ -71,7 +92,17 @@ LLAMA13B_CAUSAL_FWDBWD = Workload("b8h40n4096d128_f16_causal_fwdbwd", 8, 40, 409
 SLIDING_N32768 = Workload("b1h40n32768d128_bf16_sliding4096", 1, 40, 32768, 128, "bf16",
                           "sliding", 4096, 0, seed=5)
 
-ALL = (SINGLE_HEAD_N256, FULL_N4096, CAUSAL_OUTLIERS_N4096, LLAMA13B_CAUSAL_FWDBWD, SLIDING_N32768)
+# Grouped-query and packed variable-length workloads (P1 §5's extensions):
+# LLaMA-3-8B's attention shape (32 query heads, 8 key/value heads, d = 128),
+# fixed-length and as a packed batch of mixed-length sequences.
+GQA_CAUSAL_FWDBWD = Workload("b4h32kv8n4096d128_bf16_causal_gqa_fwdbwd", 4, 32, 4096, 128, "bf16",
+                             "causal", 0, 0, seed=7, backward=True, H_kv=8)
+PACKED_CAUSAL_FWDBWD = Workload("h32kv8t32768d128_bf16_causal_packed128to8192_fwdbwd", 1, 32,
+                                32768, 128, "bf16", "causal", 0, 0, seed=8, backward=True, H_kv=8,
+                                packed_lo=128, packed_hi=8192, packed_seed=6)
+
+ALL = (SINGLE_HEAD_N256, FULL_N4096, CAUSAL_OUTLIERS_N4096, LLAMA13B_CAUSAL_FWDBWD, SLIDING_N32768,
+       GQA_CAUSAL_FWDBWD, PACKED_CAUSAL_FWDBWD)
 BY_NAME = {w.name: w for w in ALL}
 
 
@@ -147,7 +178,14 @@ def length_mix(total: int, lo: int, hi: int, seed: int) -> list:
 
 
 def make_inputs(w: Workload) -> dict:
-    """The seeded inputs of a named workload (CPU tensors)."""
+    """The seeded inputs of a named workload (CPU tensors); packed workloads also
+    hold ``cu_seqlens`` (int32 row offsets)."""
+    if w.packed:
+        out = draw_packed(w.H, w.kv_heads, w.N, w.d, w.dtype, w.seed, with_do=w.backward)
+        out["cu_seqlens"] = torch.from_numpy(packed_offsets(w.lengths))
+        return out
+    if w.kv_heads != w.H:
+        return draw_grouped(w.B, w.H, w.kv_heads, w.N, w.d, w.dtype, w.seed, with_do=w.backward)
     return draw(w.B, w.H, w.N, w.d, w.dtype, w.seed, with_do=w.backward,
                 outlier_frac=w.outlier_frac, outlier_mul=w.outlier_mul)
 
