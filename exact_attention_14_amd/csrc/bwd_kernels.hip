@@ -142,9 +142,9 @@ void bwd_dq_kernel(BwdParams p, int n_qblk) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int64_t head, qblk;
   if (p.g.cu_seqlens == nullptr)
-    fwd_work_item(blockIdx.x, p.n_heads, n_qblk, MASK, &head, &qblk);
+    fwd_item(blockIdx.x, p.n_heads, n_qblk, MASK, &head, &qblk);
   else
-    packed_work_item(blockIdx.x, p.g.H, p.n_heads / p.g.H, n_qblk, false, &head, &qblk);
+    packed_item(blockIdx.x, p.g.H, p.n_heads / p.g.H, n_qblk, false, &head, &qblk);
   // The query head's rows (a packed sequence's blocks past its end exit) and
   // its key/value head.
   const HeadRows hr = query_rows(p.g, head);
@@ -308,11 +308,10 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int64_t head, kblk;
   if (p.g.cu_seqlens == nullptr) {
-    kv_work_item(blockIdx.x, p.n_kv_heads, n_kblk, MASK, &head, &kblk);
+    kv_item(blockIdx.x, p.n_kv_heads, n_kblk, MASK, &head, &kblk);
   } else {
     const int H_kv = p.g.H / p.g.group;
-    packed_work_item(blockIdx.x, H_kv, p.n_kv_heads / H_kv, n_kblk, MASK == kCausal, &head,
-                     &kblk);
+    packed_item(blockIdx.x, H_kv, p.n_kv_heads / H_kv, n_kblk, MASK == kCausal, &head, &kblk);
   }
   // The key/value head's rows (a packed sequence's blocks past its end exit)
   // and its group of query heads, whose contributions all accumulate here.

@@ -108,9 +108,9 @@ void fwd_kernel(FwdParams p) {
 
   int64_t head, qblk;
   if (p.g.cu_seqlens == nullptr)
-    fwd_work_item(blockIdx.x, p.n_heads, p.n_qblk, MASK, &head, &qblk);
+    fwd_item(blockIdx.x, p.n_heads, p.n_qblk, MASK, &head, &qblk);
   else
-    packed_work_item(blockIdx.x, p.g.H, p.n_heads / p.g.H, p.n_qblk, false, &head, &qblk);
+    packed_item(blockIdx.x, p.g.H, p.n_heads / p.g.H, p.n_qblk, false, &head, &qblk);
   // The head's rows: all N of a fixed-length batch, or one packed sequence
   // (whose query blocks past its end have nothing to do).  K and V come from
   // the head's key/value head.

@@ -58,18 +58,46 @@ hipError_t launch_fwd(const FwdParams& p, int dt_bf16, int d, int mode, int64_t 
 hipError_t launch_bwd(const BwdParams& p, int dt_bf16, int d, int mode, hipStream_t stream);
 
 // The rows of query head x (device side: reads the packed batch's offsets).
-__device__ __forceinline__ HeadRows query_rows(const HeadGeom& g, int64_t x) {
-  if (g.cu_seqlens == nullptr) return query_head_rows(x, g.H, g.group, g.rows, false, 0, 0);
-  const int64_t s = x / g.H;
-  return query_head_rows(x, g.H, g.group, g.rows, true, g.cu_seqlens[s], g.cu_seqlens[s + 1]);
+__device__ __forceinline__ HeadRows query_rows(const HeadGeom& g, uint32_t x) {
+  const uint32_t H = g.H, group = g.group, rows = g.rows;
+  if (g.cu_seqlens == nullptr) return query_head_rows<uint32_t>(x, H, group, rows, false, 0, 0);
+  const uint32_t s = x / H;
+  return query_head_rows<uint32_t>(x, H, group, rows, true, g.cu_seqlens[s], g.cu_seqlens[s + 1]);
 }
 
 // The rows of key/value head y and its query heads (device side).
-__device__ __forceinline__ KvHeadRows kv_rows(const HeadGeom& g, int64_t y) {
-  const int H_kv = g.H / g.group;
-  if (g.cu_seqlens == nullptr) return kv_head_rows(y, H_kv, g.group, g.rows, false, 0, 0);
-  const int64_t s = y / H_kv;
-  return kv_head_rows(y, H_kv, g.group, g.rows, true, g.cu_seqlens[s], g.cu_seqlens[s + 1]);
+__device__ __forceinline__ KvHeadRows kv_rows(const HeadGeom& g, uint32_t y) {
+  const uint32_t group = g.group, H_kv = g.H / g.group, rows = g.rows;
+  if (g.cu_seqlens == nullptr) return kv_head_rows<uint32_t>(y, H_kv, group, rows, false, 0, 0);
+  const uint32_t s = y / H_kv;
+  return kv_head_rows<uint32_t>(y, H_kv, group, rows, true, g.cu_seqlens[s], g.cu_seqlens[s + 1]);
+}
+
+// Work items of fixed-length batches (device side, 32-bit arithmetic).
+__device__ __forceinline__ void fwd_item(uint32_t wg, uint32_t n_heads, uint32_t n_blk, int mode,
+                                         int64_t* head, int64_t* blk) {
+  uint32_t h, b;
+  fwd_work_item<uint32_t>(wg, n_heads, n_blk, mode, &h, &b);
+  *head = h;
+  *blk = b;
+}
+
+__device__ __forceinline__ void kv_item(uint32_t wg, uint32_t n_heads, uint32_t n_blk, int mode,
+                                        int64_t* head, int64_t* blk) {
+  uint32_t h, b;
+  kv_work_item<uint32_t>(wg, n_heads, n_blk, mode, &h, &b);
+  *head = h;
+  *blk = b;
+}
+
+// Work item of a packed batch (device side, 32-bit arithmetic).
+__device__ __forceinline__ void packed_item(uint32_t wg, uint32_t heads, uint32_t n_seqs,
+                                            uint32_t n_blk, bool ascending, int64_t* head,
+                                            int64_t* blk) {
+  uint32_t h, b;
+  packed_work_item<uint32_t>(wg, heads, n_seqs, n_blk, ascending, &h, &b);
+  *head = h;
+  *blk = b;
 }
 
 }  // namespace attn

@@ -131,19 +131,24 @@ struct HeadRows {
   int64_t q_row0, kv_row0, len;
 };
 
-ATTN_HD HeadRows query_head_rows(int64_t x, int64_t H, int64_t group, int64_t rows, bool packed,
-                                 int64_t seq_lo, int64_t seq_hi) {
-  const int64_t outer = x / H, h = x % H, kvh = h / group, H_kv = H / group;
+// The index arithmetic is a template on the integer type: the host checks use
+// int64_t, the kernels uint32_t (all indices are below 2^31 after
+// validation; 32-bit divisions are far shorter on the GPU than 64-bit ones,
+// whose code measurably slowed the whole kernel).  Row offsets are 64-bit.
+template <typename I>
+ATTN_HD HeadRows query_head_rows(I x, I H, I group, I rows, bool packed, int64_t seq_lo,
+                                 int64_t seq_hi) {
+  const I outer = x / H, h = x - outer * H, kvh = h / group, H_kv = H / group;
   HeadRows r;
   if (!packed) {
-    r.q_row0 = x * rows;
-    r.kv_row0 = (outer * H_kv + kvh) * rows;
+    r.q_row0 = static_cast<int64_t>(x) * rows;
+    r.kv_row0 = (static_cast<int64_t>(outer) * H_kv + kvh) * rows;
     r.len = rows;
   } else {
     const int64_t lo = imin(imax(seq_lo, 0), rows);
     const int64_t hi = imin(imax(seq_hi, lo), rows);
-    r.q_row0 = h * rows + lo;
-    r.kv_row0 = kvh * rows + lo;
+    r.q_row0 = static_cast<int64_t>(h) * rows + lo;
+    r.kv_row0 = static_cast<int64_t>(kvh) * rows + lo;
     r.len = hi - lo;
   }
   return r;
@@ -156,20 +161,21 @@ struct KvHeadRows {
   int64_t kv_row0, q_row0, q_stride, len;
 };
 
-ATTN_HD KvHeadRows kv_head_rows(int64_t y, int64_t H_kv, int64_t group, int64_t rows, bool packed,
-                                int64_t seq_lo, int64_t seq_hi) {
-  const int64_t outer = y / H_kv, kvh = y % H_kv, H = H_kv * group;
+template <typename I>
+ATTN_HD KvHeadRows kv_head_rows(I y, I H_kv, I group, I rows, bool packed, int64_t seq_lo,
+                                int64_t seq_hi) {
+  const I outer = y / H_kv, kvh = y - outer * H_kv, H = H_kv * group;
   KvHeadRows r;
   if (!packed) {
-    r.kv_row0 = y * rows;
-    r.q_row0 = (outer * H + kvh * group) * rows;
+    r.kv_row0 = static_cast<int64_t>(y) * rows;
+    r.q_row0 = (static_cast<int64_t>(outer) * H + static_cast<int64_t>(kvh) * group) * rows;
     r.q_stride = rows;
     r.len = rows;
   } else {
     const int64_t lo = imin(imax(seq_lo, 0), rows);
     const int64_t hi = imin(imax(seq_hi, lo), rows);
-    r.kv_row0 = kvh * rows + lo;
-    r.q_row0 = kvh * group * rows + lo;
+    r.kv_row0 = static_cast<int64_t>(kvh) * rows + lo;
+    r.q_row0 = static_cast<int64_t>(kvh) * group * rows + lo;
     r.q_stride = rows;
     r.len = hi - lo;
   }
@@ -179,21 +185,22 @@ ATTN_HD KvHeadRows kv_head_rows(int64_t y, int64_t H_kv, int64_t group, int64_t 
 // Workgroup id -> work item.  The hardware deals consecutive workgroup ids
 // round-robin to the kNumXcd dies; this bijection gives die x a contiguous
 // run of work items, so all query blocks of a head share one die's L2.
-ATTN_HD int64_t xcd_remap(int64_t wg, int64_t n_wg) {
-  int64_t per = n_wg / kNumXcd, rem = n_wg % kNumXcd;
-  int64_t xcd = wg % kNumXcd, slot = wg / kNumXcd;
-  int64_t start = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
+template <typename I>
+ATTN_HD I xcd_remap(I wg, I n_wg) {
+  const I per = n_wg / kNumXcd, rem = n_wg % kNumXcd;
+  const I xcd = wg % kNumXcd, slot = wg / kNumXcd;
+  const I start = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
   return start + slot;
 }
 
 // Work item -> (head, query block).  With a causal mask the query blocks of
 // a head run last-first: they visit the most key tiles, so starting them
 // first shortens the tail of the launch.
-ATTN_HD void fwd_work_item(int64_t wg, int64_t n_heads, int64_t n_qblk, int mode, int64_t* head,
-                           int64_t* qblk) {
-  int64_t item = xcd_remap(wg, n_heads * n_qblk);
+template <typename I>
+ATTN_HD void fwd_work_item(I wg, I n_heads, I n_qblk, int mode, I* head, I* qblk) {
+  const I item = xcd_remap<I>(wg, n_heads * n_qblk);
   *head = item / n_qblk;
-  int64_t qb = item % n_qblk;
+  const I qb = item - *head * n_qblk;
   *qblk = (mode == kCausal) ? (n_qblk - 1 - qb) : qb;
 }
 
@@ -210,21 +217,21 @@ ATTN_HD void fwd_work_item(int64_t wg, int64_t n_heads, int64_t n_qblk, int mode
 // when `ascending` (a causal key block's work shrinks with its index).  For
 // other head counts the order is the same block by block, over all heads,
 // dealt round-robin to the dies.
-ATTN_HD void packed_work_item(int64_t wg, int64_t heads, int64_t n_seqs, int64_t n_blk,
-                              bool ascending, int64_t* head, int64_t* blk) {
-  const int64_t per_blk = heads * n_seqs;
-  int64_t b, s, h;
+template <typename I>
+ATTN_HD void packed_work_item(I wg, I heads, I n_seqs, I n_blk, bool ascending, I* head, I* blk) {
+  const I per_blk = heads * n_seqs;
+  I b, s, h;
   if (heads % kNumXcd == 0) {
-    const int64_t hp = heads / kNumXcd, xcd = wg % kNumXcd, slot = wg / kNumXcd;
+    const I hp = heads / kNumXcd, xcd = wg % kNumXcd, slot = wg / kNumXcd;
     b = slot / (hp * n_seqs);
-    const int64_t rem = slot % (hp * n_seqs);
+    const I rem = slot - b * (hp * n_seqs);
     s = rem / hp;
-    h = xcd * hp + rem % hp;
+    h = xcd * hp + (rem - s * hp);
   } else {
     b = wg / per_blk;
-    const int64_t rem = wg % per_blk;
+    const I rem = wg - b * per_blk;
     s = rem / heads;
-    h = rem % heads;
+    h = rem - s * heads;
   }
   *head = s * heads + h;
   *blk = ascending ? b : n_blk - 1 - b;
@@ -239,13 +246,13 @@ ATTN_HD void packed_work_item(int64_t wg, int64_t heads, int64_t n_seqs, int64_t
 // about the same work and keep the head-major order of fwd_work_item, where
 // the blocks of a head run side by side and share its streamed Q/dO tiles in
 // L2.
-ATTN_HD void kv_work_item(int64_t wg, int64_t n_heads, int64_t n_kblk, int mode, int64_t* head,
-                          int64_t* kblk) {
+template <typename I>
+ATTN_HD void kv_work_item(I wg, I n_heads, I n_kblk, int mode, I* head, I* kblk) {
   if (mode == kCausal) {
-    *head = wg % n_heads;
     *kblk = wg / n_heads;
+    *head = wg - *kblk * n_heads;
   } else {
-    fwd_work_item(wg, n_heads, n_kblk, kNone, head, kblk);
+    fwd_work_item<I>(wg, n_heads, n_kblk, kNone, head, kblk);
   }
 }
 

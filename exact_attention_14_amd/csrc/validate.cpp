@@ -260,7 +260,7 @@ attn_status attn_fwd_workgroup(int64_t wg, int64_t n_heads, int64_t n_qblk, attn
       n_heads * n_qblk > attn::kMaxI32 || wg < 0 || wg >= n_heads * n_qblk)
     return ATTN_E_SHAPE;
   if (attn::check_mask(mode, 0, 0) != ATTN_OK) return ATTN_E_MASK;
-  attn::fwd_work_item(wg, n_heads, n_qblk, mode, head, qblk);
+  attn::fwd_work_item<int64_t>(wg, n_heads, n_qblk, mode, head, qblk);
   return ATTN_OK;
 }
 
@@ -271,7 +271,7 @@ attn_status attn_bwd_kv_workgroup(int64_t wg, int64_t n_heads, int64_t n_kblk,
       n_heads * n_kblk > attn::kMaxI32 || wg < 0 || wg >= n_heads * n_kblk)
     return ATTN_E_SHAPE;
   if (attn::check_mask(mode, 0, 0) != ATTN_OK) return ATTN_E_MASK;
-  attn::kv_work_item(wg, n_heads, n_kblk, mode, head, kblk);
+  attn::kv_work_item<int64_t>(wg, n_heads, n_kblk, mode, head, kblk);
   return ATTN_OK;
 }
 

@@ -152,7 +152,7 @@ int main() {
           std::vector<int64_t> last_blk(kNumXcd, asc ? -1 : n_blk);
           for (int64_t w = 0; w < n; ++w) {
             int64_t x, b;
-            packed_work_item(w, heads, n_seqs, n_blk, asc != 0, &x, &b);
+            packed_work_item<int64_t>(w, heads, n_seqs, n_blk, asc != 0, &x, &b);
             CHECK(x >= 0 && x < heads * n_seqs && b >= 0 && b < n_blk, "packed item range");
             if (x < 0 || x >= heads * n_seqs || b < 0 || b >= n_blk) continue;
             seen[b * heads * n_seqs + x]++;
@@ -175,18 +175,18 @@ int main() {
       const int64_t group = H / H_kv, B = 3, rows = 5;
       for (int64_t b = 0; b < B; ++b)
         for (int64_t h = 0; h < H; ++h) {
-          const HeadRows r = query_head_rows(b * H + h, H, group, rows, false, 0, 0);
+          const HeadRows r = query_head_rows<int64_t>(b * H + h, H, group, rows, false, 0, 0);
           CHECK(r.q_row0 == (b * H + h) * rows && r.len == rows, "fixed q rows H=%lld", (long long)H);
           CHECK(r.kv_row0 == (b * H_kv + h / group) * rows, "fixed kv head H=%lld H_kv=%lld",
                 (long long)H, (long long)H_kv);
         }
       for (int64_t y = 0; y < B * H_kv; ++y) {
-        const KvHeadRows k = kv_head_rows(y, H_kv, group, rows, false, 0, 0);
+        const KvHeadRows k = kv_head_rows<int64_t>(y, H_kv, group, rows, false, 0, 0);
         CHECK(k.kv_row0 == y * rows && k.len == rows, "fixed kv rows");
         for (int64_t g = 0; g < group; ++g) {
           // member g of the group is the query head that reads this key/value head
           const int64_t x = (y / H_kv) * H + (y % H_kv) * group + g;
-          const HeadRows r = query_head_rows(x, H, group, rows, false, 0, 0);
+          const HeadRows r = query_head_rows<int64_t>(x, H, group, rows, false, 0, 0);
           CHECK(r.kv_row0 == k.kv_row0 && r.q_row0 == k.q_row0 + g * k.q_stride, "fixed group");
         }
       }
@@ -204,7 +204,7 @@ int main() {
           if (H % H_kv) continue;
           const int64_t group = H / H_kv, n_seqs = 2;
           for (int64_t x = 0; x < n_seqs * H; ++x) {
-            const HeadRows r = query_head_rows(x, H, group, T, true, o[0], o[1]);
+            const HeadRows r = query_head_rows<int64_t>(x, H, group, T, true, o[0], o[1]);
             const int64_t h = x % H;
             CHECK(r.len >= 0 && r.q_row0 >= h * T && r.q_row0 + r.len <= (h + 1) * T,
                   "packed q rows inside head");
@@ -215,13 +215,13 @@ int main() {
               CHECK(r.q_row0 == h * T + o[0] && r.len == o[1] - o[0], "well-formed offsets");
           }
           for (int64_t y = 0; y < n_seqs * H_kv; ++y) {
-            const KvHeadRows k = kv_head_rows(y, H_kv, group, T, true, o[0], o[1]);
+            const KvHeadRows k = kv_head_rows<int64_t>(y, H_kv, group, T, true, o[0], o[1]);
             const int64_t kvh = y % H_kv;
             CHECK(k.len >= 0 && k.kv_row0 >= kvh * T && k.kv_row0 + k.len <= (kvh + 1) * T,
                   "packed kv-major rows inside head");
             for (int64_t g = 0; g < group; ++g) {
               const int64_t h = kvh * group + g;
-              const HeadRows r = query_head_rows((y / H_kv) * H + h, H, group, T, true, o[0], o[1]);
+              const HeadRows r = query_head_rows<int64_t>((y / H_kv) * H + h, H, group, T, true, o[0], o[1]);
               CHECK(r.q_row0 == k.q_row0 + g * k.q_stride && r.kv_row0 == k.kv_row0 &&
                         r.len == k.len, "packed group member");
             }

@@ -94,15 +94,18 @@ SLIDING_N32768 = Workload("b1h40n32768d128_bf16_sliding4096", 1, 40, 32768, 128,
 
 # Grouped-query and packed variable-length workloads (P1 §5's extensions):
 # LLaMA-3-8B's attention shape (32 query heads, 8 key/value heads, d = 128),
-# fixed-length and as a packed batch of mixed-length sequences.
+# fixed-length and as a packed batch of mixed-length sequences, and the same
+# query shape with one shared key/value head (multi-query attention).
 GQA_CAUSAL_FWDBWD = Workload("b4h32kv8n4096d128_bf16_causal_gqa_fwdbwd", 4, 32, 4096, 128, "bf16",
                              "causal", 0, 0, seed=7, backward=True, H_kv=8)
+MQA_CAUSAL_FWDBWD = Workload("b4h32kv1n4096d128_bf16_causal_mqa_fwdbwd", 4, 32, 4096, 128, "bf16",
+                             "causal", 0, 0, seed=9, backward=True, H_kv=1)
 PACKED_CAUSAL_FWDBWD = Workload("h32kv8t32768d128_bf16_causal_packed128to8192_fwdbwd", 1, 32,
                                 32768, 128, "bf16", "causal", 0, 0, seed=8, backward=True, H_kv=8,
                                 packed_lo=128, packed_hi=8192, packed_seed=6)
 
 ALL = (SINGLE_HEAD_N256, FULL_N4096, CAUSAL_OUTLIERS_N4096, LLAMA13B_CAUSAL_FWDBWD, SLIDING_N32768,
-       GQA_CAUSAL_FWDBWD, PACKED_CAUSAL_FWDBWD)
+       GQA_CAUSAL_FWDBWD, MQA_CAUSAL_FWDBWD, PACKED_CAUSAL_FWDBWD)
 BY_NAME = {w.name: w for w in ALL}
 
 
