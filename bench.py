@@ -186,8 +186,12 @@ def main():
     backward = None
     if w.backward:
         do = inp["do"].to("cuda")
-        ws = torch.empty(max(ea.attn_bwd_workspace_bytes(q.dtype, w.B, w.H, w.N, w.d), 16),
-                         dtype=torch.uint8, device="cuda")
+        if w.packed:
+            need = ea.attn_bwd_varlen_workspace_bytes(q.dtype, len(w.lengths), max_len, w.N, w.H,
+                                                      w.kv_heads, w.d)
+        else:
+            need = ea.attn_bwd_workspace_bytes(q.dtype, w.B, w.H, w.N, w.d, w.kv_heads)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
 
         def bstep():
             if w.packed:

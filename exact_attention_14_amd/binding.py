@@ -27,7 +27,8 @@ STATUS = {0: "ATTN_OK", 1: "ATTN_E_NULLPTR", 2: "ATTN_E_SHAPE", 3: "ATTN_E_UNSUP
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str",
            "attn_fwd_check", "attn_bwd_check", "attn_fwd_tiles", "attn_kv_tile_range",
            "attn_fwd_workgroup", "attn_bwd_kv_workgroup", "attn_fwd_gqa", "attn_bwd_gqa",
-           "attn_fwd_varlen", "attn_bwd_varlen")
+           "attn_fwd_varlen", "attn_bwd_varlen", "attn_bwd_gqa_workspace_bytes",
+           "attn_bwd_varlen_workspace_bytes")
 
 
 class AttnError(RuntimeError):
@@ -68,6 +69,10 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd_varlen.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, i64, i64,
                                   i64, i64, i64, i64, f32, i32, i64, i64, vp]
     L.attn_bwd_varlen.restype = i32
+    L.attn_bwd_gqa_workspace_bytes.argtypes = [i32, i64, i64, i64, i64, i64]
+    L.attn_bwd_gqa_workspace_bytes.restype = sz
+    L.attn_bwd_varlen_workspace_bytes.argtypes = [i32, i64, i64, i64, i64, i64, i64]
+    L.attn_bwd_varlen_workspace_bytes.restype = sz
     L.attn_bwd_workspace_bytes.argtypes = [i32, i64, i64, i64, i64]
     L.attn_bwd_workspace_bytes.restype = sz
     L.attn_status_str.argtypes = [i32]
@@ -197,9 +202,22 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, mask=None, sc
     return out, lse
 
 
-def attn_bwd_workspace_bytes(dtype: torch.dtype, B: int, H: int, N: int, d: int) -> int:
-    dt = ATTN_BF16 if dtype == torch.bfloat16 else ATTN_F16
-    return int(lib().attn_bwd_workspace_bytes(dt, B, H, N, d))
+def _code(dtype: torch.dtype) -> int:
+    return ATTN_BF16 if dtype == torch.bfloat16 else ATTN_F16
+
+
+def attn_bwd_workspace_bytes(dtype: torch.dtype, B: int, H: int, N: int, d: int,
+                             H_kv: int | None = None) -> int:
+    """Workspace bytes of attn_bwd (or, with H_kv < H, of its grouped-query form)."""
+    if H_kv is None or H_kv == H:
+        return int(lib().attn_bwd_workspace_bytes(_code(dtype), B, H, N, d))
+    return int(lib().attn_bwd_gqa_workspace_bytes(_code(dtype), B, H, H_kv, N, d))
+
+
+def attn_bwd_varlen_workspace_bytes(dtype: torch.dtype, n_seqs: int, max_seqlen: int, total: int,
+                                    H: int, H_kv: int, d: int) -> int:
+    return int(lib().attn_bwd_varlen_workspace_bytes(_code(dtype), n_seqs, max_seqlen, total, H,
+                                                     H_kv, d))
 
 
 def attn_bwd(q, k, v, o, lse, do, *, mask=None, scale=None, workspace=None):
@@ -223,7 +241,7 @@ def attn_bwd(q, k, v, o, lse, do, *, mask=None, scale=None, workspace=None):
         scale = 1.0 / math.sqrt(d)
     mode, wl, wr = mask_args(mask)
     dt = _dtype_code(q)
-    need = attn_bwd_workspace_bytes(q.dtype, B, H, N, d)
+    need = attn_bwd_workspace_bytes(q.dtype, B, H, N, d, H_kv)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     elif workspace.device != q.device or not workspace.is_contiguous():
@@ -324,7 +342,7 @@ def attn_bwd_varlen(q, k, v, o, lse, do, cu_seqlens, max_seqlen: int, *, mask=No
         scale = 1.0 / math.sqrt(d)
     mode, wl, wr = mask_args(mask)
     dt = _dtype_code(q)
-    need = attn_bwd_workspace_bytes(q.dtype, 1, H, T, d)
+    need = attn_bwd_varlen_workspace_bytes(q.dtype, n_seqs, int(max_seqlen), T, H, H_kv, d)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
     elif workspace.device != q.device or not workspace.is_contiguous():

@@ -6,7 +6,8 @@
 // and relies on recomputation).  With lse saved by the forward, a tile of P
 // is exp(scale * q.k - lse) directly -- no running max is needed.
 //
-// Two launches, no atomics, so the result is deterministic:
+// Two launches (three with split groups), no atomics, so the result is
+// deterministic:
 //   1. bwd_dq:      query-major like the forward.  D_i = dO_i . O_i from the
 //                   forward's stored O (fp32), written negated for the
 //                   second pass together with each row's score offset
@@ -21,6 +22,12 @@
 //                   registers; each wavefront owns 64 keys (two blocks that
 //                   share every operand read from LDS) with its dV and dK
 //                   accumulators in AGPRs, one wavefront per SIMD.
+//                   With grouped-query heads a key/value head's workgroup
+//                   walks the query heads of its group (P1 §5 names
+//                   grouped-query attention).  When there are too few
+//                   key/value heads to fill the chip, each group is split
+//                   into slices with one workgroup each, and
+//   3. bwd_kv_reduce: sums the slices' fp32 partial dK/dV in slice order.
 // Tiles stream through double-buffered LDS stages filled by direct
 // HBM-to-LDS loads (one array per stage, so reading one stage never waits
 // for the loads into the other).  Each 64-row tile is stored once, row-major
@@ -306,15 +313,21 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, half = lane >> 5, r32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Workgroups come in kv_split runs of (key/value head, key block) items;
+  // run `slice` takes that share of each group's query heads.
+  const uint32_t n_items = static_cast<uint32_t>(p.n_kv_heads) * n_kblk;
+  const uint32_t slice = blockIdx.x / n_items, item = blockIdx.x - slice * n_items;
   int64_t head, kblk;
   if (p.g.cu_seqlens == nullptr) {
-    kv_item(blockIdx.x, p.n_kv_heads, n_kblk, MASK, &head, &kblk);
+    kv_item(item, p.n_kv_heads, n_kblk, MASK, &head, &kblk);
   } else {
     const int H_kv = p.g.H / p.g.group;
-    packed_item(blockIdx.x, H_kv, p.n_kv_heads / H_kv, n_kblk, MASK == kCausal, &head, &kblk);
+    packed_item(item, H_kv, p.n_kv_heads / H_kv, n_kblk, MASK == kCausal, &head, &kblk);
   }
+  const int g_per = p.g.group / p.kv_split;
+  const int g0 = static_cast<int>(slice) * g_per, g1 = g0 + g_per;
   // The key/value head's rows (a packed sequence's blocks past its end exit)
-  // and its group of query heads, whose contributions all accumulate here.
+  // and its query heads g0 .. g1-1, whose contributions accumulate here.
   const KvHeadRows kr = kv_rows(p.g, head);
   const int N = static_cast<int>(kr.len);
   const int k0 = static_cast<int>(kblk) * BK;
@@ -467,7 +480,7 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
   // The query tiles of each query head of the group in turn (one head
   // without grouping); every tile ends with a barrier, so the next head's
   // first loads may refill stage 0.
-  for (int gq = 0; gq < p.g.group; ++gq) {
+  for (int gq = g0; gq < g1; ++gq) {
     const size_t qoff = static_cast<size_t>(kr.q_row0 + gq * kr.q_stride) * ROWB;
     const size_t soff = static_cast<size_t>(kr.q_row0 + gq * kr.q_stride);
     const auto rQ = make_rsrc(reinterpret_cast<const char*>(p.Q) + qoff, head_bytes);
@@ -501,9 +514,33 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
   }
 
   // K entered the products with a negative scale's sign flip, so
-  // dK = scale * dS^T Q with the signed scale; dV = P^T dO.
+  // dK = scale * dS^T Q with the signed scale; dV = P^T dO.  A split group
+  // leaves its fp32 partial sums (unscaled) for the reduction instead.
   acc_fence(dv);
   acc_fence(dk);
+  if (p.kv_split > 1) {
+    const size_t part = (static_cast<size_t>(slice) * p.kv_rows + kr.kv_row0) * D;
+    const uint32_t part_bytes = static_cast<uint32_t>(N) * D * 4;
+    const auto rpK = make_rsrc(p.dK_part + part, part_bytes);
+    const auto rpV = make_rsrc(p.dV_part + part, part_bytes);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x16_t& a_ = dk[kb * DBLK + db];
+          const f32x16_t& b_ = dv[kb * DBLK + db];
+          const uint32_t off = (static_cast<uint32_t>(kcol[kb]) * D + db * 32 + g * 8 + half * 4) * 4;
+          buf_store16(u32x4_t{__float_as_uint(a_[g * 4 + 0]), __float_as_uint(a_[g * 4 + 1]),
+                              __float_as_uint(a_[g * 4 + 2]), __float_as_uint(a_[g * 4 + 3])},
+                      rpK, off);
+          buf_store16(u32x4_t{__float_as_uint(b_[g * 4 + 0]), __float_as_uint(b_[g * 4 + 1]),
+                              __float_as_uint(b_[g * 4 + 2]), __float_as_uint(b_[g * 4 + 3])},
+                      rpV, off);
+        }
+    return;
+  }
   const float sc = p.scale;
   const auto rdK = make_rsrc(reinterpret_cast<char*>(p.dK) + kvoff, head_bytes);
   const auto rdV = make_rsrc(reinterpret_cast<char*>(p.dV) + kvoff, head_bytes);
@@ -526,6 +563,38 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
       }
 }
 
+// ------------------------------------------------------ split reduction
+// dK = scale * sum of the slices' partial dK, dV = sum of the partial dV,
+// added in slice order (deterministic), rounded once.  Eight consecutive
+// elements per thread; the key/value side is [kv_rows, D] row-major.
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(BwdParams p, int64_t n_elems) {
+  const int64_t e0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 8;
+  if (e0 >= n_elems) return;
+  float k[8], v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) k[i] = v[i] = 0.0f;
+  for (int s = 0; s < p.kv_split; ++s) {
+    const float4* pk = reinterpret_cast<const float4*>(p.dK_part + s * n_elems + e0);
+    const float4* pv = reinterpret_cast<const float4*>(p.dV_part + s * n_elems + e0);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float4 a = pk[h], b = pv[h];
+      k[4 * h + 0] += a.x; k[4 * h + 1] += a.y; k[4 * h + 2] += a.z; k[4 * h + 3] += a.w;
+      v[4 * h + 0] += b.x; v[4 * h + 1] += b.y; v[4 * h + 2] += b.z; v[4 * h + 3] += b.w;
+    }
+  }
+  const float sc = p.scale;
+  u32x4_t ok, ov;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ok[i] = Elem<T>::pack2(k[2 * i] * sc, k[2 * i + 1] * sc);
+    ov[i] = Elem<T>::pack2(v[2 * i], v[2 * i + 1]);
+  }
+  *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(p.dK) + e0 * 2) = ok;
+  *reinterpret_cast<u32x4_t*>(reinterpret_cast<char*>(p.dV) + e0 * 2) = ov;
+}
+
 template <typename T, int D, int MASK>
 hipError_t launch_all(const BwdParams& p, hipStream_t stream) {
   const int n_qblk = static_cast<int>(ceil_div(p.max_len, kBwdDqBlockQ));
@@ -537,8 +606,16 @@ hipError_t launch_all(const BwdParams& p, hipStream_t stream) {
 
   const int n_kblk = static_cast<int>(ceil_div(p.max_len, kBwdKvBlockK));
   hipLaunchKernelGGL((bwd_dkdv_kernel<T, D, MASK>),
-                     dim3(static_cast<unsigned>(static_cast<int64_t>(p.n_kv_heads) * n_kblk)),
+                     dim3(static_cast<unsigned>(static_cast<int64_t>(p.n_kv_heads) * n_kblk *
+                                                p.kv_split)),
                      dim3(kBwdThreads), 0, stream, p, n_kblk);
+  e = hipGetLastError();
+  if (e != hipSuccess || p.kv_split == 1) return e;
+
+  const int64_t n_elems = p.kv_rows * D;
+  hipLaunchKernelGGL((bwd_kv_reduce_kernel<T>),
+                     dim3(static_cast<unsigned>(ceil_div(n_elems, 8 * 256))), dim3(256), 0, stream,
+                     p, n_elems);
   return hipGetLastError();
 }
 

@@ -157,6 +157,9 @@ __device__ __forceinline__ void buf_store8(u32x2_t v, __amdgpu_buffer_rsrc_t r, 
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), r,
                                         static_cast<int>(voff), 0, 0);
 }
+__device__ __forceinline__ void buf_store16(u32x4_t v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(voff), 0, 0);
+}
 __device__ __forceinline__ void buf_store4(float v, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
   __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, static_cast<int>(voff), 0, 0);
 }

@@ -46,6 +46,10 @@ struct BwdParams {
   int n_heads;    // query heads of the dQ launch: B * H, or n_seqs * H
   int n_kv_heads; // key/value heads of the dK/dV launch: B * H_kv, or n_seqs * H_kv
   int max_len;    // longest sequence (N of a fixed-length batch)
+  int kv_split;   // slices of each group of query heads in the dK/dV pass
+  float* dK_part; // kv_split > 1: fp32 partial dK, [kv_split][kv_rows][d] (workspace)
+  float* dV_part; // likewise for dV
+  int64_t kv_rows;  // rows of the key/value side (B*H_kv*N, or H_kv*T)
   int wl, wr;
   float c;        // |scale| * log2(e), at least 1e-30
   float scale;    // the signed scale (applied to dQ and dK)

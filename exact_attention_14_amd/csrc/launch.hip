@@ -68,9 +68,15 @@ attn_status bwd_impl(attn_dtype dt, const void* Q, const void* K, const void* V,
   BwdParams p{};
   p.Q = Q; p.K = K; p.V = V; p.O = O; p.lse = lse; p.dO = dO;
   p.dQ = dQ; p.dK = dK; p.dV = dV;
+  const uint64_t row_bytes = row_array_bytes(1, 1, g.q_rows());
   p.Dneg = static_cast<float*>(workspace);
-  p.Loff = reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                    row_array_bytes(1, 1, g.q_rows()));
+  p.Loff = reinterpret_cast<float*>(static_cast<char*>(workspace) + row_bytes);
+  p.kv_split = static_cast<int>(kv_split(g));
+  p.kv_rows = g.kv_rows();
+  if (p.kv_split > 1) {
+    p.dK_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + 2 * row_bytes);
+    p.dV_part = p.dK_part + static_cast<size_t>(p.kv_split) * g.kv_rows() * g.d;
+  }
   p.g = head_geom(g, cu_seqlens);
   p.n_heads = static_cast<int>(g.n_heads());
   p.n_kv_heads = static_cast<int>(g.n_kv_heads());

@@ -98,6 +98,26 @@ uint64_t workspace_bytes(int64_t B, int64_t H, int64_t N) {
   return 2u * row_array_bytes(B, H, N);
 }
 
+int64_t kv_split(const Geometry& g) {
+  const int64_t group = g.H / g.H_kv;
+  if (group == 1) return 1;
+  // Key blocks that hold rows (for a packed batch at least the total rows'
+  // worth) times key/value heads; aim for two workgroups per compute unit.
+  constexpr int64_t kTarget = 512;
+  const int64_t blocks = g.packed ? ceil_div(g.rows, kBwdKvBlockK) * g.H_kv
+                                  : g.outer * g.H_kv * ceil_div(g.rows, kBwdKvBlockK);
+  for (int64_t s = 1; s < group; ++s)
+    if (group % s == 0 && blocks * s >= kTarget) return s;
+  return group;
+}
+
+uint64_t bwd_workspace_bytes(const Geometry& g) {
+  const uint64_t rows = 2u * row_array_bytes(1, 1, g.q_rows());
+  const int64_t split = kv_split(g);
+  if (split == 1) return rows;
+  return rows + 2u * static_cast<uint64_t>(split) * g.kv_rows() * g.d * 4u;
+}
+
 namespace {
 
 // Tensor sizes of a call: query side, key/value side, per-row float32.
@@ -155,7 +175,7 @@ attn_status bwd_check_g(int dt, const void* Q, const void* K, const void* V, con
   attn_status s = check_geometry(dt, g);
   if (s != ATTN_OK) return s;
   const Sizes z = sizes_of(g);
-  const uint64_t wb = 2u * row_array_bytes(1, 1, g.q_rows());
+  const uint64_t wb = bwd_workspace_bytes(g);
   TensorArgs a = base_args(dt, g, scale, mode, wl, wr);
   a.n_in = 6;
   a.in[0] = Q; a.in[1] = K; a.in[2] = V; a.in[3] = O; a.in[4] = lse; a.in[5] = dO;
@@ -212,6 +232,20 @@ const char* attn_status_str(attn_status s) {
 size_t attn_bwd_workspace_bytes(attn_dtype dt, int64_t B, int64_t H, int64_t N, int64_t d) {
   if (attn::check_sizes(dt, B, H, N, d) != ATTN_OK) return 0;
   return static_cast<size_t>(attn::workspace_bytes(B, H, N));
+}
+
+size_t attn_bwd_gqa_workspace_bytes(attn_dtype dt, int64_t B, int64_t H, int64_t H_kv, int64_t N,
+                                    int64_t d) {
+  const attn::Geometry g = attn::fixed_geometry(B, H, H_kv, N, d);
+  if (attn::check_geometry(dt, g) != ATTN_OK) return 0;
+  return static_cast<size_t>(attn::bwd_workspace_bytes(g));
+}
+
+size_t attn_bwd_varlen_workspace_bytes(attn_dtype dt, int64_t n_seqs, int64_t max_seqlen,
+                                       int64_t total, int64_t H, int64_t H_kv, int64_t d) {
+  const attn::Geometry g{n_seqs, H, H_kv, total, max_seqlen, d, true};
+  if (attn::check_geometry(dt, g) != ATTN_OK) return 0;
+  return static_cast<size_t>(attn::bwd_workspace_bytes(g));
 }
 
 attn_status attn_fwd_check(attn_dtype dt, const void* Q, const void* K, const void* V,

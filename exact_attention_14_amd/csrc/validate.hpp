@@ -52,6 +52,16 @@ inline uint64_t row_array_bytes(int64_t B, int64_t H, int64_t N) {
 }
 uint64_t workspace_bytes(int64_t B, int64_t H, int64_t N);
 
+// The backward's key-major pass runs one workgroup per (key/value head, key
+// block) and walks the query heads of its group.  With few key/value heads
+// (multi-query attention) that leaves the chip idle, so the group is split
+// into kv_split(g) slices (a divisor of the group), one workgroup each, whose
+// fp32 partial dK/dV a reduction sums in slice order.
+int64_t kv_split(const Geometry& g);
+// Workspace of a backward call: the per-row arrays, then (when split) the
+// partial dK and dV, [kv_split][kv rows][d] float32 each.
+uint64_t bwd_workspace_bytes(const Geometry& g);
+
 // Validation of a forward / backward call on any geometry (cu_seqlens is
 // read only for a packed batch).
 attn_status fwd_check_g(int dt, const void* Q, const void* K, const void* V, const void* O,

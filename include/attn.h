@@ -165,8 +165,6 @@ attn_status attn_bwd(attn_dtype dt, const void* Q, const void* K, const void* V,
  *   n_seqs      >= 1;  max_seqlen in [1, T];  total = T >= 1.
  * The size rules of the conventions apply with B*H*N replaced by
  * n_seqs*H*max_seqlen for the thread bound and by H*T for the tensor sizes.
- * The backward's workspace is attn_bwd_workspace_bytes(dt, 1, H, T, d)
- * (two float32 values per query-side row, as for attn_bwd).
  */
 
 /* attn_fwd_gqa -- attn_fwd with K, V of shape [B, H_kv, N, d]. */
@@ -178,8 +176,9 @@ attn_status attn_fwd_gqa(attn_dtype dt, const void* Q, const void* K, const void
 /*
  * attn_bwd_gqa -- attn_bwd with K, V, dK, dV of shape [B, H_kv, N, d]:
  * dK and dV of a key/value head sum the contributions of all the query
- * heads that read it (deterministic, no atomics).  Workspace:
- * attn_bwd_workspace_bytes(dt, B, H, N, d).
+ * heads that read it (deterministic, no atomics: with few key/value heads
+ * the query heads of a group are split into slices whose fp32 partial sums
+ * are added in a fixed order).  Workspace: attn_bwd_gqa_workspace_bytes.
  */
 attn_status attn_bwd_gqa(attn_dtype dt, const void* Q, const void* K, const void* V,
                          const void* O, const float* lse, const void* dO, void* dQ, void* dK,
@@ -194,7 +193,19 @@ attn_status attn_fwd_varlen(attn_dtype dt, const void* Q, const void* K, const v
                             int64_t d, float scale, attn_mask_mode mode, int64_t window_left,
                             int64_t window_right, void* stream);
 
-/* attn_bwd_varlen -- backward over a packed variable-length batch (see above). */
+/*
+ * attn_bwd_gqa_workspace_bytes / attn_bwd_varlen_workspace_bytes -- device
+ * workspace attn_bwd_gqa / attn_bwd_varlen need: the per-row arrays of
+ * attn_bwd plus, when the library splits the query heads of a group, fp32
+ * partial dK and dV.  Return 0 for invalid sizes.  Pure host functions.
+ */
+size_t attn_bwd_gqa_workspace_bytes(attn_dtype dt, int64_t B, int64_t H, int64_t H_kv, int64_t N,
+                                    int64_t d);
+size_t attn_bwd_varlen_workspace_bytes(attn_dtype dt, int64_t n_seqs, int64_t max_seqlen,
+                                       int64_t total, int64_t H, int64_t H_kv, int64_t d);
+
+/* attn_bwd_varlen -- backward over a packed variable-length batch (see above);
+ * workspace: attn_bwd_varlen_workspace_bytes. */
 attn_status attn_bwd_varlen(attn_dtype dt, const void* Q, const void* K, const void* V,
                             const void* O, const float* lse, const void* dO, void* dQ, void* dK,
                             void* dV, void* workspace, size_t workspace_bytes,

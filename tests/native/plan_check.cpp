@@ -288,8 +288,12 @@ int main() {
     CHECK(fwd_check_g(ATTN_F16, q, gk, gv, go, gl, reinterpret_cast<const int32_t*>(q + 12288), pg, 0.1f, 1, 0, 0) == ATTN_E_ALIAS, "packed cu under lse");
     CHECK(fwd_check_g(ATTN_F16, q, gk, gv, go, gl, cu, Geometry{3, 4, 1, 8, 9, 64, true}, 0.1f, 1, 0, 0) == ATTN_E_SHAPE, "max_len > T");
     CHECK(fwd_check_g(ATTN_F16, q, gk, gv, go, gl, cu, Geometry{0, 4, 1, 8, 5, 64, true}, 0.1f, 1, 0, 0) == ATTN_E_SHAPE, "no sequences");
-    const size_t pws = attn_bwd_workspace_bytes(ATTN_F16, 1, 4, 8, 64);
-    void* W2 = q + 20480;
+    // H = 4 query heads on one key/value head with a single key block: the
+    // group is split in 4, so the workspace adds 2 x 4 x 8 x 64 fp32 partials.
+    const size_t pws = attn_bwd_varlen_workspace_bytes(ATTN_F16, 3, 5, 8, 4, 1, 64);
+    CHECK(pws == 2 * 256 + 2 * 4 * 8 * 64 * 4, "packed split workspace %zu", pws);
+    CHECK(attn_bwd_gqa_workspace_bytes(ATTN_F16, 1, 4, 4, 8, 64) == attn_bwd_workspace_bytes(ATTN_F16, 1, 4, 8, 64), "no split without groups");
+    void* W2 = q + 40960;
     CHECK(bwd_check_g(ATTN_F16, q, gk, gv, go, gl, go, q + 24576, q + 28672, q + 30720, W2, pws, cu, pg, 0.1f, 1, 0, 0) == ATTN_OK, "packed bwd ok");
     CHECK(bwd_check_g(ATTN_F16, q, gk, gv, go, gl, go, q + 24576, q + 28672, q + 30720, W2, pws - 4, cu, pg, 0.1f, 1, 0, 0) == ATTN_E_WORKSPACE, "packed bwd ws");
     CHECK(bwd_check_g(ATTN_F16, q, gk, gv, go, gl, go, q + 24576, q + 28672, q + 28672 + 512, W2, pws, cu, pg, 0.1f, 1, 0, 0) == ATTN_E_ALIAS, "packed dK/dV overlap");

@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     lib = ea.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -83,8 +83,8 @@ def test_grouped_and_packed_entry_points_reject_bad_arguments_before_any_hip_cal
     assert lib.attn_fwd_varlen(*vargs(cu, 0, 4, 8)) == 2
     assert lib.attn_fwd_varlen(*vargs(L, 2, 4, 8)) == 7
     assert lib.attn_fwd_varlen(*vargs(cu, 2, 4, 8, 96)) == 3
-    # backward: workspace below attn_bwd_workspace_bytes(dt, 1, H, T, d)
-    ws = ea.attn_bwd_workspace_bytes(__import__("torch").float16, 1, 2, 8, 64)
+    # backward: workspace below attn_bwd_varlen_workspace_bytes
+    ws = ea.attn_bwd_varlen_workspace_bytes(__import__("torch").float16, 2, 4, 8, 2, 1, 64)
     b = [0, Q, K, V, O, L, O, base + 24576, base + 28672, base + 32768, base + 36864, ws - 4,
          cu, 2, 4, 8, 2, 1, 64, 0.1, 1, 0, 0, None]
     assert lib.attn_bwd_varlen(*b) == 8
@@ -92,6 +92,25 @@ def test_grouped_and_packed_entry_points_reject_bad_arguments_before_any_hip_cal
          1, 6, 4, 8, 64, 0.1, 1, 0, 0, None]
     assert lib.attn_bwd_gqa(*g) == 2
     assert bytes(buf) == b"\0" * len(buf)
+
+
+def test_grouped_workspace_sizes():
+    """Per-row arrays as for attn_bwd; split groups (few key/value heads) add fp32 partials."""
+    import torch
+    f16 = torch.float16
+    rows = lambda n: 2 * ((n * 4 + 255) // 256 * 256)
+    # 512 key blocks with H_kv = 8 at B4 N4096: no split, same as standard attention
+    assert ea.attn_bwd_workspace_bytes(f16, 4, 32, 4096, 128, 8) == rows(4 * 32 * 4096)
+    assert ea.attn_bwd_workspace_bytes(f16, 4, 32, 4096, 128, 8) == \
+        ea.attn_bwd_workspace_bytes(f16, 4, 32, 4096, 128)
+    # multi-query at B4 N4096: 64 key blocks, split into 8 slices of 4 query heads
+    assert ea.attn_bwd_workspace_bytes(f16, 4, 32, 4096, 128, 1) == \
+        rows(4 * 32 * 4096) + 2 * 8 * (4 * 1 * 4096) * 128 * 4
+    # a group of 3 with 1 block: split 3 (the only divisor reaching the target)
+    assert ea.attn_bwd_workspace_bytes(f16, 1, 3, 100, 64, 1) == rows(300) + 2 * 3 * 100 * 64 * 4
+    # packed: T = 32768 rows, H_kv = 8 -> 1024 blocks, no split
+    assert ea.attn_bwd_varlen_workspace_bytes(f16, 15, 8192, 32768, 32, 8, 128) == rows(32 * 32768)
+    assert ea.attn_bwd_varlen_workspace_bytes(f16, 2, 9, 8, 2, 1, 64) == 0  # max_seqlen > T
 
 
 def test_binding_rejects_mismatched_grouped_and_packed_shapes():
