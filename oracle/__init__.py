@@ -17,7 +17,8 @@ Sources (cited as P1..P4 with their sections throughout this package):
       templates (epilogue mask variants: none / causal / sliding window).
 
 Grouped-query heads and packed variable-length batches (P1 §5's
-extensions) are in ``grouped.py``.
+extensions) are in ``grouped.py``; decoding over a paged K/V cache in
+``decode.py``.
 
 Every function here is pinned by ``tests/test_oracle_*.py`` against closed
 forms, invariants, brute force on tiny inputs and an independent library
@@ -25,9 +26,11 @@ routine (torch's CPU float64 scaled-dot-product attention and autograd).
 """
 from .attention import (MASK_MODES, allowed_matrix, allowed_count, forward_head, forward_rows,
                         forward, backward_head, backward)
+from .decode import forward_decode, gather
 from .grouped import (backward_gqa, backward_varlen, forward_gqa, forward_varlen, group_size)
 from .online import online_forward_head
 
 __all__ = ["MASK_MODES", "allowed_matrix", "allowed_count", "forward_head", "forward_rows",
            "forward", "backward_head", "backward", "online_forward_head", "group_size",
-           "forward_gqa", "backward_gqa", "forward_varlen", "backward_varlen"]
+           "forward_gqa", "backward_gqa", "forward_varlen", "backward_varlen", "forward_decode",
+           "gather"]
