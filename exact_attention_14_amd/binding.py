@@ -28,7 +28,7 @@ EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str"
            "attn_fwd_check", "attn_bwd_check", "attn_fwd_tiles", "attn_kv_tile_range",
            "attn_fwd_workgroup", "attn_bwd_kv_workgroup", "attn_fwd_gqa", "attn_bwd_gqa",
            "attn_fwd_varlen", "attn_bwd_varlen", "attn_bwd_gqa_workspace_bytes",
-           "attn_bwd_varlen_workspace_bytes")
+           "attn_bwd_varlen_workspace_bytes", "attn_decode", "attn_decode_workspace_bytes")
 
 
 class AttnError(RuntimeError):
@@ -73,6 +73,11 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd_gqa_workspace_bytes.restype = sz
     L.attn_bwd_varlen_workspace_bytes.argtypes = [i32, i64, i64, i64, i64, i64, i64]
     L.attn_bwd_varlen_workspace_bytes.restype = sz
+    L.attn_decode.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64, i64,
+                              i64, i64, i64, i64, f32, i32, i64, i64, vp]
+    L.attn_decode.restype = i32
+    L.attn_decode_workspace_bytes.argtypes = [i32, i64, i64, i64, i64, i64, i64]
+    L.attn_decode_workspace_bytes.restype = sz
     L.attn_bwd_workspace_bytes.argtypes = [i32, i64, i64, i64, i64]
     L.attn_bwd_workspace_bytes.restype = sz
     L.attn_status_str.argtypes = [i32]
@@ -385,3 +390,63 @@ def attn_bwd_kv_workgroup(wg, n_heads, n_kblk, mode):
     st = lib().attn_bwd_kv_workgroup(wg, n_heads, n_kblk, mode, ctypes.byref(h), ctypes.byref(kb))
     _raise("attn_bwd_kv_workgroup", st)
     return h.value, kb.value
+
+
+def attn_decode_workspace_bytes(dtype: torch.dtype, n_seqs: int, H: int, H_kv: int, n_q: int,
+                                d: int, max_seqlen: int) -> int:
+    return int(lib().attn_decode_workspace_bytes(_code(dtype), n_seqs, H, H_kv, n_q, d, max_seqlen))
+
+
+def attn_decode(q, k_cache, v_cache, block_table, seq_lens, max_seqlen: int, *, mask=None,
+                scale=None, out=None, lse=None, workspace=None):
+    """Split-KV decoding over a paged cache; returns (O [n_seqs, H, n_q, d], lse [n_seqs, H, n_q]).
+
+    q: [n_seqs, H, n_q, d]; k_cache, v_cache: [n_pages, H_kv, page_size, d] page pools;
+    block_table: int32 [n_seqs, max_pages]; seq_lens: int32 [n_seqs] (cache lengths, each at
+    least n_q and at most ``max_seqlen``).  The n_q query tokens of a sequence sit at its last
+    n_q cache positions; masks count cache positions.
+    """
+    if q.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("q must be [n_seqs, H, n_q, d] and the caches [n_pages, H_kv, page_size, d]")
+    n_seqs, H, n_q, d = q.shape
+    n_pages, H_kv, page_size, dk = k_cache.shape
+    _check_gpu(q)
+    for name, t, shape in (("q", q, tuple(q.shape)), ("k_cache", k_cache, tuple(k_cache.shape)),
+                           ("v_cache", v_cache, tuple(k_cache.shape))):
+        if tuple(t.shape) != shape or t.dtype != q.dtype or t.device != q.device \
+                or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous {q.dtype} {shape} on {q.device}")
+    if dk != d:
+        raise ValueError("q and the caches must have the same head size")
+    if (block_table.dim() != 2 or block_table.shape[0] != n_seqs or block_table.dtype != torch.int32
+            or block_table.device != q.device or not block_table.is_contiguous()):
+        raise ValueError(f"block_table must be a contiguous int32 [n_seqs, max_pages] on {q.device}")
+    if (tuple(seq_lens.shape) != (n_seqs,) or seq_lens.dtype != torch.int32
+            or seq_lens.device != q.device or not seq_lens.is_contiguous()):
+        raise ValueError(f"seq_lens must be a contiguous int32 [n_seqs] on {q.device}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    mode, wl, wr = mask_args(mask)
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    elif tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError(f"out must be contiguous {q.dtype} {tuple(q.shape)}")
+    if lse is None:
+        lse = torch.empty((n_seqs, H, n_q), dtype=torch.float32, device=q.device)
+    elif (tuple(lse.shape) != (n_seqs, H, n_q) or lse.dtype != torch.float32
+          or not lse.is_contiguous() or lse.device != q.device):
+        raise ValueError(f"lse must be contiguous float32 [n_seqs, H, n_q] on {q.device}")
+    need = attn_decode_workspace_bytes(q.dtype, n_seqs, H, H_kv, n_q, d, int(max_seqlen))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    with torch.cuda.device(q.device):
+        st = lib().attn_decode(dt, q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                               block_table.data_ptr(), seq_lens.data_ptr(), out.data_ptr(),
+                               lse.data_ptr(), ws_ptr, ws_bytes, n_seqs, H, H_kv, n_q, d,
+                               page_size, n_pages, block_table.shape[1], int(max_seqlen),
+                               float(scale), mode, wl, wr, _stream_ptr(q.device))
+    _raise("attn_decode", st)
+    return out, lse

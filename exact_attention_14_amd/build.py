@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 
 ARCH = "gfx950"
-HIP_SOURCES = ["fwd_kernel.hip", "bwd_kernels.hip", "launch.hip"]
+HIP_SOURCES = ["fwd_kernel.hip", "bwd_kernels.hip", "decode_kernel.hip", "launch.hip"]
 # The backward's key-major kernel keeps its dV/dK accumulators in AGPRs
 # (inline-asm matrix instructions) and its score tiles in VGPRs; the
 # compiler's own matrix instructions must then use the VGPR form, or it would

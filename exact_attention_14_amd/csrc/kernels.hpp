@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "decode.hpp"
 #include "plan.hpp"
 
 namespace attn {
@@ -60,6 +61,7 @@ struct BwdParams {
 hipError_t launch_fwd(const FwdParams& p, int dt_bf16, int d, int mode, int64_t n_wg,
                       hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, int dt_bf16, int d, int mode, hipStream_t stream);
+hipError_t launch_decode(const DecParams& p, int dt_bf16, int d, int mode, hipStream_t stream);
 
 // The rows of query head x (device side: reads the packed batch's offsets).
 __device__ __forceinline__ HeadRows query_rows(const HeadGeom& g, uint32_t x) {

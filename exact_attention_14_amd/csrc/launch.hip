@@ -1,5 +1,6 @@
 // launch.hip -- the C ABI entry points that enqueue work: attn_fwd / attn_bwd and
-// their grouped-query (_gqa) and packed variable-length (_varlen) variants.
+// their grouped-query (_gqa) and packed variable-length (_varlen) variants, and
+// split-KV decoding over a paged cache (attn_decode).
 // Validation lives in validate.cpp and runs before any HIP call.
 #include <hip/hip_runtime.h>
 
@@ -158,6 +159,52 @@ attn_status attn_bwd_varlen(attn_dtype dt, const void* Q, const void* K, const v
   return attn::bwd_impl(dt, Q, K, V, O, lse, dO, dQ, dK, dV, workspace, workspace_bytes,
                         cu_seqlens, attn::packed_geometry(n_seqs, max_seqlen, total, H, H_kv, d),
                         scale, mode, window_left, window_right, stream);
+}
+
+attn_status attn_decode(attn_dtype dt, const void* Q, const void* K_cache, const void* V_cache,
+                        const int32_t* block_table, const int32_t* seq_lens, void* O, float* lse,
+                        void* workspace, size_t workspace_bytes, int64_t n_seqs, int64_t H,
+                        int64_t H_kv, int64_t n_q, int64_t d, int64_t page_size, int64_t n_pages,
+                        int64_t max_pages_per_seq, int64_t max_seqlen, float scale,
+                        attn_mask_mode mode, int64_t window_left, int64_t window_right,
+                        void* stream) {
+  const attn::DecodeGeometry g{n_seqs, H, H_kv, n_q, d, page_size, n_pages, max_pages_per_seq,
+                               max_seqlen};
+  attn_status s = attn::decode_check(dt, Q, K_cache, V_cache, block_table, seq_lens, O, lse,
+                                     workspace, workspace_bytes, g, scale, mode, window_left,
+                                     window_right);
+  if (s != ATTN_OK) return s;
+  attn::DecParams p{};
+  p.Q = Q; p.K = K_cache; p.V = V_cache; p.O = O; p.lse = lse;
+  p.block_table = block_table; p.seq_lens = seq_lens;
+  p.n_seqs = static_cast<int>(n_seqs);
+  p.H = static_cast<int>(H);
+  p.H_kv = static_cast<int>(H_kv);
+  p.group = static_cast<int>(H / H_kv);
+  p.n_q = static_cast<int>(n_q);
+  p.page_size = static_cast<int>(page_size);
+  p.n_pages = static_cast<int>(n_pages);
+  p.max_pages = static_cast<int>(max_pages_per_seq);
+  const int64_t rt = attn::dec_row_tiles(H / H_kv, n_q);
+  int64_t n_splits, chunk;
+  attn::dec_plan(n_seqs, H_kv, rt, max_seqlen, &n_splits, &chunk);
+  p.row_tiles = static_cast<int>(rt);
+  p.n_splits = static_cast<int>(n_splits);
+  p.chunk = static_cast<int>(chunk);
+  if (n_splits > 1) {
+    const uint64_t parts = static_cast<uint64_t>(n_seqs) * H_kv * rt * n_splits;
+    p.part_o = static_cast<float*>(workspace);
+    p.part_lse = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          (parts * attn::kDecRows * d * 4u + 255u) / 256u * 256u);
+  }
+  const int64_t cap = max_pages_per_seq * page_size;
+  p.wl = mode == ATTN_MASK_SLIDING ? attn::clip_window(window_left, cap) : 0;
+  p.wr = mode == ATTN_MASK_SLIDING ? attn::clip_window(window_right, cap) : 0;
+  p.c = attn::exp2_coeff(scale);
+  p.qsign = scale < 0.0f ? 0x80008000u : 0u;
+  hipError_t e = attn::launch_decode(p, dt == ATTN_BF16, static_cast<int>(d), mode,
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
 
 }  // extern "C"

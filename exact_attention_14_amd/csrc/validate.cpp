@@ -6,6 +6,7 @@
 #include <cstring>
 
 #include "attn.h"
+#include "decode.hpp"
 #include "plan.hpp"
 #include "validate.hpp"
 
@@ -69,6 +70,11 @@ attn_status check_mask(int mode, int64_t wl, int64_t wr) {
 attn_status check_common(const TensorArgs& a) {
   attn_status s = check_geometry(a.dt, a.g);
   if (s != ATTN_OK) return s;
+  return check_buffers(a);
+}
+
+attn_status check_buffers(const TensorArgs& a) {
+  attn_status s;
   for (int i = 0; i < a.n_in; ++i)
     if (a.in[i] == nullptr) return ATTN_E_NULLPTR;
   for (int i = 0; i < a.n_out; ++i)
@@ -194,6 +200,80 @@ attn_status bwd_check_g(int dt, const void* Q, const void* K, const void* V, con
   return ATTN_OK;
 }
 
+attn_status decode_sizes(int dt, const DecodeGeometry& g) {
+  if (dt != ATTN_F16 && dt != ATTN_BF16) return ATTN_E_UNSUPPORTED;
+  if (g.d != 64 && g.d != 128) return ATTN_E_UNSUPPORTED;
+  // Pages hold whole 64-key tiles.
+  if (g.page_size < kDecTileK || g.page_size % kDecTileK != 0) return ATTN_E_UNSUPPORTED;
+  if (g.n_seqs < 1 || g.H < 1 || g.H_kv < 1 || g.n_q < 1 || g.n_pages < 1 || g.max_pages < 1 ||
+      g.max_seqlen < 1)
+    return ATTN_E_SHAPE;
+  if (g.n_seqs > kMaxI32 || g.H > kMaxI32 || g.n_q > kMaxI32 || g.page_size > kMaxI32 ||
+      g.n_pages > kMaxI32 || g.max_pages > kMaxI32)
+    return ATTN_E_SHAPE;
+  if (g.H_kv > g.H || g.H % g.H_kv != 0) return ATTN_E_SHAPE;
+  // Positions within a sequence are 32-bit; the longest sequence fits its pages.
+  if (g.max_pages > kMaxI32 / g.page_size) return ATTN_E_SHAPE;
+  if (g.max_seqlen > g.max_pages * g.page_size) return ATTN_E_SHAPE;
+  if (g.n_seqs > kMaxI32 / g.max_pages) return ATTN_E_SHAPE;
+  // Tensor sizes stay far below 2^62 bytes.
+  const int64_t group = g.H / g.H_kv;
+  if (g.n_seqs * g.H > kMaxI32 / g.n_q) return ATTN_E_SHAPE;
+  if (g.n_pages > (int64_t(1) << 62) / (g.H_kv * g.page_size * g.d * 2)) return ATTN_E_SHAPE;
+  // Grid of the decode launch and thread count of the combine launch.
+  const int64_t rt = dec_row_tiles(group, g.n_q);
+  int64_t n_splits, chunk;
+  dec_plan(g.n_seqs, g.H_kv, rt, g.max_seqlen, &n_splits, &chunk);
+  if (g.n_seqs * g.H_kv * rt > kMaxI32 / n_splits) return ATTN_E_SHAPE;
+  if (g.n_seqs * g.H_kv * rt * kDecRows * (g.d / 8) > (int64_t(1) << 32) - 256) return ATTN_E_SHAPE;
+  return ATTN_OK;
+}
+
+uint64_t decode_workspace_bytes(int64_t n_seqs, int64_t H, int64_t H_kv, int64_t n_q, int64_t d,
+                                int64_t max_seqlen) {
+  const int64_t rt = dec_row_tiles(H / H_kv, n_q);
+  int64_t n_splits, chunk;
+  dec_plan(n_seqs, H_kv, rt, max_seqlen, &n_splits, &chunk);
+  if (n_splits == 1) return 0;
+  const uint64_t parts = static_cast<uint64_t>(n_seqs) * H_kv * rt * n_splits;
+  // partial O [parts][32][d], then partial lse [parts][32], 256-byte aligned
+  const uint64_t o_bytes = (parts * kDecRows * d * 4u + 255u) / 256u * 256u;
+  return o_bytes + parts * kDecRows * 4u;
+}
+
+attn_status decode_check(int dt, const void* Q, const void* K, const void* V,
+                         const int32_t* block_table, const int32_t* seq_lens, const void* O,
+                         const float* lse, const void* ws, size_t ws_bytes,
+                         const DecodeGeometry& g, float scale, int mode, int64_t wl, int64_t wr) {
+  attn_status s = decode_sizes(dt, g);
+  if (s != ATTN_OK) return s;
+  const uint64_t q_bytes = static_cast<uint64_t>(g.n_seqs) * g.H * g.n_q * g.d * 2u;
+  const uint64_t pool_bytes = static_cast<uint64_t>(g.n_pages) * g.H_kv * g.page_size * g.d * 2u;
+  const uint64_t wb = decode_workspace_bytes(g.n_seqs, g.H, g.H_kv, g.n_q, g.d, g.max_seqlen);
+  TensorArgs a{};
+  a.dt = dt; a.scale = scale; a.mode = mode; a.wl = wl; a.wr = wr;
+  for (int i = 0; i < 8; ++i) a.in_align[i] = 16;
+  a.n_in = 5;
+  a.in[0] = Q; a.in[1] = K; a.in[2] = V; a.in[3] = block_table; a.in[4] = seq_lens;
+  a.in_bytes[0] = q_bytes; a.in_bytes[1] = a.in_bytes[2] = pool_bytes;
+  a.in_bytes[3] = static_cast<uint64_t>(g.n_seqs) * g.max_pages * 4u;
+  a.in_bytes[4] = static_cast<uint64_t>(g.n_seqs) * 4u;
+  a.in_align[3] = a.in_align[4] = 4;
+  a.n_out = 2;
+  a.out[0] = O; a.out[1] = lse;
+  a.out_bytes[0] = q_bytes;
+  a.out_bytes[1] = static_cast<uint64_t>(g.n_seqs) * g.H * g.n_q * 4u;
+  if (wb > 0) {  // the workspace is read only when the keys are split
+    a.out[2] = ws;
+    a.out_bytes[2] = wb;
+    a.n_out = 3;
+  }
+  s = check_buffers(a);
+  if (s != ATTN_OK) return s;
+  if (ws_bytes < wb) return ATTN_E_WORKSPACE;
+  return ATTN_OK;
+}
+
 attn_status fwd_check(int dt, const void* Q, const void* K, const void* V, const void* O,
                       const float* lse, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
                       int mode, int64_t wl, int64_t wr) {
@@ -246,6 +326,15 @@ size_t attn_bwd_varlen_workspace_bytes(attn_dtype dt, int64_t n_seqs, int64_t ma
   const attn::Geometry g{n_seqs, H, H_kv, total, max_seqlen, d, true};
   if (attn::check_geometry(dt, g) != ATTN_OK) return 0;
   return static_cast<size_t>(attn::bwd_workspace_bytes(g));
+}
+
+size_t attn_decode_workspace_bytes(attn_dtype dt, int64_t n_seqs, int64_t H, int64_t H_kv,
+                                   int64_t n_q, int64_t d, int64_t max_seqlen) {
+  // The page parameters do not affect the split; any valid ones will do.
+  const attn::DecodeGeometry g{n_seqs, H, H_kv, n_q, d, attn::kDecTileK, 1,
+                               attn::ceil_div(max_seqlen, attn::kDecTileK), max_seqlen};
+  if (attn::decode_sizes(dt, g) != ATTN_OK) return 0;
+  return static_cast<size_t>(attn::decode_workspace_bytes(n_seqs, H, H_kv, n_q, d, max_seqlen));
 }
 
 attn_status attn_fwd_check(attn_dtype dt, const void* Q, const void* K, const void* V,

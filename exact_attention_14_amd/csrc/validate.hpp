@@ -45,6 +45,9 @@ attn_status check_sizes(int dt, int64_t B, int64_t H, int64_t N, int64_t d);
 attn_status check_geometry(int dt, const Geometry& g);
 attn_status check_mask(int mode, int64_t wl, int64_t wr);
 attn_status check_common(const TensorArgs& a);
+// Pointers, mask, scale, alignment and aliasing of a call (check_common
+// without the geometry).
+attn_status check_buffers(const TensorArgs& a);
 // Bytes of one float32 value per row, padded to 256.
 inline uint64_t row_array_bytes(int64_t B, int64_t H, int64_t N) {
   const uint64_t rows = static_cast<uint64_t>(B) * H * N;
@@ -72,6 +75,19 @@ attn_status bwd_check_g(int dt, const void* Q, const void* K, const void* V, con
                         const void* dV, const void* ws, size_t ws_bytes,
                         const int32_t* cu_seqlens, const Geometry& g, float scale, int mode,
                         int64_t wl, int64_t wr);
+
+// Split-KV decoding over a paged cache (decode.hpp): validation, and the
+// workspace (fp32 partial O and lse per split) it needs.
+struct DecodeGeometry {
+  int64_t n_seqs, H, H_kv, n_q, d, page_size, n_pages, max_pages, max_seqlen;
+};
+attn_status decode_sizes(int dt, const DecodeGeometry& g);
+uint64_t decode_workspace_bytes(int64_t n_seqs, int64_t H, int64_t H_kv, int64_t n_q, int64_t d,
+                                int64_t max_seqlen);
+attn_status decode_check(int dt, const void* Q, const void* K, const void* V,
+                         const int32_t* block_table, const int32_t* seq_lens, const void* O,
+                         const float* lse, const void* ws, size_t ws_bytes,
+                         const DecodeGeometry& g, float scale, int mode, int64_t wl, int64_t wr);
 
 attn_status fwd_check(int dt, const void* Q, const void* K, const void* V, const void* O,
                       const float* lse, int64_t B, int64_t H, int64_t N, int64_t d, float scale,

@@ -214,6 +214,50 @@ attn_status attn_bwd_varlen(attn_dtype dt, const void* Q, const void* K, const v
                             attn_mask_mode mode, int64_t window_left, int64_t window_right,
                             void* stream);
 
+/*
+ * Split-KV decoding over a paged K/V cache (P1 §5 names split-KV decoding
+ * and paged caches among FlashAttention's extensions; the layout is this
+ * library's).  Each of n_seqs sequences contributes n_q new query tokens,
+ * which sit at the last n_q positions of its cache, and attends to its
+ * seq_lens[s] cached keys.
+ *
+ *   Q            in:  [n_seqs, H, n_q, d] of `dt`.
+ *   K_cache, V_cache  in: page pools [n_pages, H_kv, page_size, d] of `dt`;
+ *                page_size a multiple of 64.
+ *   block_table  in:  int32 [n_seqs, max_pages_per_seq], device, 4-byte
+ *                aligned: key j of sequence s is row j % page_size of page
+ *                block_table[s][j / page_size].
+ *   seq_lens     in:  int32 [n_seqs], device: cache length L_s of each
+ *                sequence, with n_q <= L_s <= max_seqlen <= max_pages_per_seq
+ *                * page_size.
+ *   O            out: [n_seqs, H, n_q, d] of `dt`; lse out: float32
+ *                [n_seqs, H, n_q], natural-log units as for attn_fwd.
+ *   workspace    device scratch of attn_decode_workspace_bytes(...) bytes
+ *                (zero when the keys are not split; then it may be NULL).
+ *   Query head h reads key/value head h / (H / H_kv) (grouped-query).
+ *   Masks use cache positions: query token i of sequence s is at position
+ *   p = L_s - n_q + i; NONE lets it see all L_s keys, CAUSAL keys j <= p,
+ *   SLIDING keys p - window_left <= j <= p + window_right.
+ * The keys are split over workgroups (chunks of whole 64-key tiles) when the
+ * sequences alone do not fill the chip; the partial results are merged by
+ * the online-softmax rule.  block_table and seq_lens live on the device and
+ * are not validated: lengths are clamped to [0, max_pages_per_seq *
+ * page_size] and page numbers to [0, n_pages), so malformed values never
+ * make the kernels access memory outside the buffers, but give unspecified
+ * results; so does L_s < n_q, or L_s > max_seqlen.  Other rules as in the
+ * conventions (ATTN_E_UNSUPPORTED also for page_size).
+ */
+size_t attn_decode_workspace_bytes(attn_dtype dt, int64_t n_seqs, int64_t H, int64_t H_kv,
+                                   int64_t n_q, int64_t d, int64_t max_seqlen);
+
+attn_status attn_decode(attn_dtype dt, const void* Q, const void* K_cache, const void* V_cache,
+                        const int32_t* block_table, const int32_t* seq_lens, void* O, float* lse,
+                        void* workspace, size_t workspace_bytes, int64_t n_seqs, int64_t H,
+                        int64_t H_kv, int64_t n_q, int64_t d, int64_t page_size, int64_t n_pages,
+                        int64_t max_pages_per_seq, int64_t max_seqlen, float scale,
+                        attn_mask_mode mode, int64_t window_left, int64_t window_right,
+                        void* stream);
+
 /* attn_status_str -- static, NUL-terminated description of a status code. */
 const char* attn_status_str(attn_status s);
 

@@ -180,6 +180,39 @@ def length_mix(total: int, lo: int, hi: int, seed: int) -> list:
     return out
 
 
+def draw_paged(lens, H: int, H_kv: int, n_q: int, d: int, dtype: str, page_size: int, seed: int,
+               spare_pages: int = 2) -> dict:
+    """Decode inputs over a paged cache: Q [n_seqs, H, n_q, d] and page pools K, V
+    [n_pages, H_kv, page_size, d] drawn in that order (sequence by sequence,
+    K then V of each); the pages of all sequences are dealt to a random
+    permutation of the pool, and every pool row no sequence owns (the tails of
+    last pages and the spare pages) is NaN, so reading one shows.  Also returns
+    block_table (int32 [n_seqs, max_pages]) and seq_lens (int32 [n_seqs])."""
+    rng = np.random.default_rng(seed)
+    n_seqs = len(lens)
+    q = rng.standard_normal((n_seqs, H, n_q, d), dtype=np.float32)
+    per = [max(1, -(-int(L) // page_size)) for L in lens]
+    n_pages = sum(per) + spare_pages
+    perm = rng.permutation(n_pages)
+    K = np.full((n_pages, H_kv, page_size, d), np.nan, dtype=np.float32)
+    V = np.full((n_pages, H_kv, page_size, d), np.nan, dtype=np.float32)
+    table = np.zeros((n_seqs, max(per)), dtype=np.int32)
+    used = 0
+    for s, L in enumerate(lens):
+        ks = rng.standard_normal((H_kv, int(L), d), dtype=np.float32)
+        vs = rng.standard_normal((H_kv, int(L), d), dtype=np.float32)
+        for pg in range(per[s]):
+            phys = int(perm[used])
+            used += 1
+            table[s, pg] = phys
+            lo, hi = pg * page_size, min(int(L), (pg + 1) * page_size)
+            K[phys, :, :hi - lo] = ks[:, lo:hi]
+            V[phys, :, :hi - lo] = vs[:, lo:hi]
+    return {"q": _round(q, dtype), "k": _round(K, dtype), "v": _round(V, dtype),
+            "block_table": torch.from_numpy(table),
+            "seq_lens": torch.from_numpy(np.asarray(lens, dtype=np.int32))}
+
+
 def make_inputs(w: Workload) -> dict:
     """The seeded inputs of a named workload (CPU tensors); packed workloads also
     hold ``cu_seqlens`` (int32 row offsets)."""
