@@ -113,6 +113,92 @@ def cpu_baseline(w, inp, budget_s: float = 12.0, max_units: int = 128):
                       f"materialised per head), {dt:.1f} s"}
 
 
+def decode_bytes(w) -> int:
+    """Algorithmic HBM bytes of one decode call: every cached K and V row of every
+    key/value head once, Q and O once, lse once."""
+    rows = sum(w.lengths)
+    kv = 2 * rows * w.kv_heads * w.d * 2
+    q_o = 2 * w.B * w.H * w.decode_q * w.d * 2
+    return kv + q_o + w.B * w.H * w.decode_q * 4
+
+
+def bench_decode(w, args, inp):
+    """Timed attn_decode calls; one JSON line with GB/s against the HBM peak."""
+    import numpy as np
+    import torch
+
+    import exact_attention_14_amd as ea
+
+    q, k, v, bt, sl = (inp[x].to("cuda") for x in ("q", "k", "v", "block_table", "seq_lens"))
+    o = torch.empty_like(q)
+    lse = torch.empty(tuple(q.shape[:-1]), dtype=torch.float32, device="cuda")
+    need = ea.attn_decode_workspace_bytes(q.dtype, w.B, w.H, w.kv_heads, w.decode_q, w.d, w.N)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+    mask = mask_arg(w)
+
+    def step():
+        ea.attn_decode(q, k, v, bt, sl, w.N, mask=mask, scale=w.scale, out=o, lse=lse,
+                       workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ta = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ms_wall = (time.perf_counter() - ta) * 1e3 / args.steps
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+    ms_kernel = evs[0].elapsed_time(evs[-1]) / args.steps
+    nbytes = decode_bytes(w)
+    value = nbytes / (ms_wall * 1e-3) / 1e9
+    achieved = nbytes / (ms_kernel * 1e-3) / 1e9
+    rec = {
+        "metric": f"attention decode GB/s of K/V cache read ({w.name})",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_wall, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded i.i.d. N(0,1) queries and cache, pages dealt to a random "
+                "permutation of the pool)",
+        "config": {"workload": w.name, "n_seqs": w.B, "H": w.H, "H_kv": w.kv_heads,
+                   "n_q": w.decode_q, "cache_len": w.N, "d": w.d, "page_size": w.page_size,
+                   "mask": w.mask, "global_batch": w.B, "seq_len": w.N, "parallelism": "none"},
+        "tokens_per_s": round(w.B * w.decode_q / (ms_wall * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_kernel", "kernel_ms": round(ms_kernel, 5),
+                     "kernel_ms_per_call": {f"p{p}": round(per[min(len(per) - 1,
+                                                                   len(per) * p // 100)], 5)
+                                            for p in (10, 50, 90)},
+                     "bytes_per_launch": nbytes},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        from workloads import to_f64
+        budget, done, t0 = 12.0, 0, time.perf_counter()
+        table, lens = inp["block_table"], inp["seq_lens"].numpy()
+        while done < w.B and time.perf_counter() - t0 < budget:
+            # the sequence's own pages, renumbered 0.., widened to fp64
+            pages = table[done].long()
+            sub = np.arange(len(pages), dtype=np.int64)[None]
+            oracle.forward_decode(to_f64(inp["q"][done:done + 1]), to_f64(inp["k"][pages]),
+                                  to_f64(inp["v"][pages]), sub, lens[done:done + 1], w.scale,
+                                  w.mask)
+            done += 1
+        dt = time.perf_counter() - t0
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        rec["cpu_baseline"] = {"value": round(nbytes * done / w.B / dt / 1e9, 4), "unit": "GB/s",
+                               "cores": int(threads), "kind": "oracle",
+                               "sample": f"{done} of {w.B} sequences, all heads (fp64 numpy), "
+                                         f"{dt:.1f} s"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -137,6 +223,9 @@ def main():
 
     w = BY_NAME[args.workload]
     inp = make_inputs(w)
+    if w.decode_q > 0:
+        bench_decode(w, args, inp)
+        return
     q, k, v = (inp[x].to("cuda") for x in ("q", "k", "v"))
     o = torch.empty_like(q)
     lse = torch.empty(tuple(q.shape[:-1]), dtype=torch.float32, device="cuda")

@@ -38,7 +38,8 @@ def kernel_source_sha() -> str:
 
 
 def _demangle_short(name: str) -> str:
-    for key in ("fwd_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "bwd_kv_reduce_kernel"):
+    for key in ("fwd_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "bwd_kv_reduce_kernel",
+                "decode_combine_kernel", "decode_kernel"):
         if key in name:
             tail = name.split(key, 1)[1]
             return key + tail.split("EEvNS")[0].replace("IDF16b", "<bf16,").replace(

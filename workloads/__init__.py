@@ -56,6 +56,10 @@ class Workload:
     packed_lo: int = 0
     packed_hi: int = 0
     packed_seed: int = 0
+    # Decoding over a paged cache: B sequences of N cached keys each, with
+    # decode_q new query tokens per sequence and pages of page_size keys.
+    decode_q: int = 0
+    page_size: int = 0
 
     @property
     def kv_heads(self) -> int:
@@ -104,8 +108,13 @@ PACKED_CAUSAL_FWDBWD = Workload("h32kv8t32768d128_bf16_causal_packed128to8192_fw
                                 32768, 128, "bf16", "causal", 0, 0, seed=8, backward=True, H_kv=8,
                                 packed_lo=128, packed_hi=8192, packed_seed=6)
 
+# Decoding: 64 sequences with 8192 cached tokens each, one new token, the
+# LLaMA-3-8B attention shape, 64-key pages.
+DECODE_CTX8192 = Workload("decode_s64h32kv8q1ctx8192d128_bf16_page64", 64, 32, 8192, 128, "bf16",
+                          "none", 0, 0, seed=10, H_kv=8, decode_q=1, page_size=64)
+
 ALL = (SINGLE_HEAD_N256, FULL_N4096, CAUSAL_OUTLIERS_N4096, LLAMA13B_CAUSAL_FWDBWD, SLIDING_N32768,
-       GQA_CAUSAL_FWDBWD, MQA_CAUSAL_FWDBWD, PACKED_CAUSAL_FWDBWD)
+       GQA_CAUSAL_FWDBWD, MQA_CAUSAL_FWDBWD, PACKED_CAUSAL_FWDBWD, DECODE_CTX8192)
 BY_NAME = {w.name: w for w in ALL}
 
 
@@ -216,6 +225,9 @@ def draw_paged(lens, H: int, H_kv: int, n_q: int, d: int, dtype: str, page_size:
 def make_inputs(w: Workload) -> dict:
     """The seeded inputs of a named workload (CPU tensors); packed workloads also
     hold ``cu_seqlens`` (int32 row offsets)."""
+    if w.decode_q > 0:
+        return draw_paged([w.N] * w.B, w.H, w.kv_heads, w.decode_q, w.d, w.dtype, w.page_size,
+                          w.seed, spare_pages=0)
     if w.packed:
         out = draw_packed(w.H, w.kv_heads, w.N, w.d, w.dtype, w.seed, with_do=w.backward)
         out["cu_seqlens"] = torch.from_numpy(packed_offsets(w.lengths))
