@@ -113,6 +113,62 @@ def test_grouped_workspace_sizes():
     assert ea.attn_bwd_varlen_workspace_bytes(f16, 2, 9, 8, 2, 1, 64) == 0  # max_seqlen > T
 
 
+def test_decode_rejects_bad_arguments_before_any_hip_call():
+    import torch
+    lib = ea.lib()
+    buf = ctypes.create_string_buffer(1 << 20)
+    base = (ctypes.addressof(buf) + 255) // 256 * 256
+    K1 = 1 << 16
+    Q, K, V, O, L = base, base + K1, base + 3 * K1, base + 5 * K1, base + 6 * K1
+    bt, sl, ws = base + 7 * K1, base + 8 * K1, base + 9 * K1
+    # n_seqs 2, H 4, H_kv 2, n_q 1, d 64, page 64, 4 pages, 2 pages per sequence, max_seqlen 128
+    good = [0, Q, K, V, bt, sl, O, L, ws, 1 << 14, 2, 4, 2, 1, 64, 64, 4, 2, 128, 0.1, 0, 0, 0, None]
+
+    def call(**kw):
+        a = list(good)
+        names = ["dt", "Q", "K", "V", "bt", "sl", "O", "L", "ws", "wsb", "n_seqs", "H", "H_kv",
+                 "n_q", "d", "page", "n_pages", "max_pages", "max_seqlen", "scale", "mode", "wl",
+                 "wr", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return lib.attn_decode(*a)
+
+    assert call(page=32) == 3            # pages hold whole 64-key tiles
+    assert call(page=96) == 3
+    assert call(d=96) == 3
+    assert call(max_seqlen=129) == 2     # beyond 2 pages of 64
+    assert call(H=6, H_kv=4) == 2
+    assert call(n_q=0) == 2
+    assert call(bt=None) == 1
+    assert call(sl=sl + 2) == 6          # int32 arrays need 4-byte alignment
+    assert call(O=Q + 16) == 7           # output overlapping an input
+    assert call(mode=2, wl=-1) == 4
+    assert call(scale=float("inf")) == 5
+    # few sequences and a long cache: the keys are split, which needs the workspace
+    need = ea.attn_decode_workspace_bytes(torch.float16, 1, 8, 1, 1, 128, 65536)
+    assert need > 0
+    wbuf = ctypes.create_string_buffer(need + 256)
+    wsp = (ctypes.addressof(wbuf) + 255) // 256 * 256
+    assert lib.attn_decode(0, Q, K, V, bt, sl, O, L, None, 0, 1, 8, 1, 1, 128, 64, 4, 1024,
+                           65536, 0.1, 0, 0, 0, None) == 1
+    assert lib.attn_decode(0, Q, K, V, bt, sl, O, L, wsp, need - 4, 1, 8, 1, 1, 128, 64, 4, 1024,
+                           65536, 0.1, 0, 0, 0, None) == 8
+    assert bytes(wbuf) == b"\0" * len(wbuf)
+    assert bytes(buf) == b"\0" * len(buf)
+
+
+def test_decode_workspace_sizes():
+    """No split (and no workspace) once sequences x key/value heads fill 512 workgroups."""
+    import torch
+    f = torch.bfloat16
+    assert ea.attn_decode_workspace_bytes(f, 64, 32, 8, 1, 128, 8192) == 0
+    # 1 sequence, 1 key/value head, 32 query rows: 128 tiles of 64 keys -> 128 splits of one tile
+    parts = 128
+    o_bytes = (parts * 32 * 128 * 4 + 255) // 256 * 256
+    assert ea.attn_decode_workspace_bytes(f, 1, 32, 1, 1, 128, 8192) == o_bytes + parts * 32 * 4
+    assert ea.attn_decode_workspace_bytes(f, 1, 6, 4, 1, 128, 100) == 0  # invalid group -> 0
+
+
 def test_binding_rejects_mismatched_grouped_and_packed_shapes():
     """Shape checks of the wrappers (CPU tensors: they raise before any GPU use)."""
     import torch
