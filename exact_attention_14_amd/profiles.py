@@ -43,7 +43,8 @@ def _demangle_short(name: str) -> str:
         if key in name:
             tail = name.split(key, 1)[1]
             return key + tail.split("EEvNS")[0].replace("IDF16b", "<bf16,").replace(
-                "IDF16_", "<f16,").replace("Li", "").replace("E", ",") + ">"
+                "IDF16_", "<f16,").replace("Lb1", "pair").replace("Lb0", "").replace(
+                "Li", "").replace("E", ",").replace(",,", ",") + ">"
     return name[:60]
 
 
