@@ -170,7 +170,8 @@ def bench_decode(w, args, inp):
         "tokens_per_s": round(w.B * w.decode_q / (ms_wall * 1e-3), 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode_kernel", "kernel_ms": round(ms_kernel, 5),
+                     "kernel": "decode_kernel" + (" + decode_combine_kernel" if need > 0 else ""),
+                     "kernel_ms": round(ms_kernel, 5),
                      "kernel_ms_per_call": {f"p{p}": round(per[min(len(per) - 1,
                                                                    len(per) * p // 100)], 5)
                                             for p in (10, 50, 90)},

@@ -113,8 +113,14 @@ PACKED_CAUSAL_FWDBWD = Workload("h32kv8t32768d128_bf16_causal_packed128to8192_fw
 DECODE_CTX8192 = Workload("decode_s64h32kv8q1ctx8192d128_bf16_page64", 64, 32, 8192, 128, "bf16",
                           "none", 0, 0, seed=10, H_kv=8, decode_q=1, page_size=64)
 
+# Long-context decoding: 4 sequences of 131072 cached tokens; 4 x 8 (sequence,
+# key/value head) items, so the keys are split over workgroups.
+DECODE_CTX131072 = Workload("decode_s4h32kv8q1ctx131072d128_bf16_page256", 4, 32, 131072, 128,
+                            "bf16", "none", 0, 0, seed=11, H_kv=8, decode_q=1, page_size=256)
+
 ALL = (SINGLE_HEAD_N256, FULL_N4096, CAUSAL_OUTLIERS_N4096, LLAMA13B_CAUSAL_FWDBWD, SLIDING_N32768,
-       GQA_CAUSAL_FWDBWD, MQA_CAUSAL_FWDBWD, PACKED_CAUSAL_FWDBWD, DECODE_CTX8192)
+       GQA_CAUSAL_FWDBWD, MQA_CAUSAL_FWDBWD, PACKED_CAUSAL_FWDBWD, DECODE_CTX8192,
+       DECODE_CTX131072)
 BY_NAME = {w.name: w for w in ALL}
 
 
