@@ -313,10 +313,10 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, half = lane >> 5, r32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // Workgroups come in kv_split runs of (key/value head, key block) items;
-  // run `slice` takes that share of each group's query heads.
-  const uint32_t n_items = static_cast<uint32_t>(p.n_kv_heads) * n_kblk;
-  const uint32_t slice = blockIdx.x / n_items, item = blockIdx.x - slice * n_items;
+  // The kv_split slices of one (key/value head, key block) item are
+  // consecutive workgroups, so the item order (heaviest first) holds across
+  // slices, and die wg % 8 keeps a fixed share of the query heads.
+  const uint32_t slice = blockIdx.x % p.kv_split, item = blockIdx.x / p.kv_split;
   int64_t head, kblk;
   if (p.g.cu_seqlens == nullptr) {
     kv_item(item, p.n_kv_heads, n_kblk, MASK, &head, &kblk);
