@@ -133,12 +133,18 @@ struct TileReaders {
 };
 
 // ------------------------------------------------------------------ dQ
-template <typename T, int D, int MASK>
-__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// PAIR (fixed-length batches with an even number of query heads per
+// key/value head): eight wavefronts, the first four on query head 2x and the
+// last four on head 2x+1 of the same key/value head, over the same 128-row
+// block, so every K/V tile brought into LDS serves both heads.
+template <typename T, int D, int MASK, bool PAIR>
+__global__ __launch_bounds__(PAIR ? 2 * kBwdThreads : kBwdThreads)
+__attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdParams p, int n_qblk) {
   using L = BwdTile<D>;
-  constexpr int BQ = kBwdDqBlockQ, BK = kBwdDqBlockK, NW = kBwdThreads / 64;
-  static_assert(BK == 64 && BQ == 32 * NW, "dQ tile geometry");
+  constexpr int BQ = kBwdDqBlockQ, BK = kBwdDqBlockK;
+  constexpr int NW = (PAIR ? 2 : 1) * kBwdThreads / 64;
+  static_assert(BK == 64 && BQ == 32 * (PAIR ? NW / 2 : NW), "dQ tile geometry");
   constexpr int KSTEPS = D / 16, DBLK = D / 32;
   constexpr uint32_t ROWB = L::ROWB;
   __shared__ __attribute__((aligned(16))) char k_lds0[L::BYTES], k_lds1[L::BYTES];
@@ -147,11 +153,18 @@ void bwd_dq_kernel(BwdParams p, int n_qblk) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, half = lane >> 5, r32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // With PAIR the wavefront's rows start at 32 * (wave % 4) within the block.
+  const int wrow = PAIR ? wave % 4 : wave;
   int64_t head, qblk;
   if (p.g.cu_seqlens == nullptr)
-    fwd_item(blockIdx.x, p.n_heads, n_qblk, MASK, &head, &qblk);
+    fwd_item(blockIdx.x, p.n_heads / (PAIR ? 2 : 1), n_qblk, MASK, &head, &qblk);
   else
     packed_item(blockIdx.x, p.g.H, p.n_heads / p.g.H, n_qblk, false, &head, &qblk);
+  if (PAIR) {
+    // item (outer, pair) -> query head outer*H + 2*pair + wave/4
+    const int64_t hp = p.g.H / 2;
+    head = (head / hp) * p.g.H + 2 * (head % hp) + wave / 4;
+  }
   // The query head's rows (a packed sequence's blocks past its end exit) and
   // its key/value head.
   const HeadRows hr = query_rows(p.g, head);
@@ -169,7 +182,7 @@ void bwd_dq_kernel(BwdParams p, int n_qblk) {
 
   // Q and dO of this lane's row stay in registers (B operands); the lane
   // holds elements kk*16 + half*8 .. +7 of the row for every kk.
-  const int wq0 = q0 + wave * 32;
+  const int wq0 = q0 + wrow * 32;
   const int qrow = wq0 + r32;
   u32x4_t qf[KSTEPS], gf[KSTEPS];
   float dsum = 0.0f;
@@ -598,9 +611,13 @@ __global__ __launch_bounds__(256) void bwd_kv_reduce_kernel(BwdParams p, int64_t
 template <typename T, int D, int MASK>
 hipError_t launch_all(const BwdParams& p, hipStream_t stream) {
   const int n_qblk = static_cast<int>(ceil_div(p.max_len, kBwdDqBlockQ));
-  hipLaunchKernelGGL((bwd_dq_kernel<T, D, MASK>),
-                     dim3(static_cast<unsigned>(static_cast<int64_t>(p.n_heads) * n_qblk)),
-                     dim3(kBwdThreads), 0, stream, p, n_qblk);
+  const int64_t n_dq = static_cast<int64_t>(p.n_heads) * n_qblk;
+  if (p.g.group % 2 == 0 && p.g.cu_seqlens == nullptr)
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, MASK, true>), dim3(static_cast<unsigned>(n_dq / 2)),
+                       dim3(2 * kBwdThreads), 0, stream, p, n_qblk);
+  else
+    hipLaunchKernelGGL((bwd_dq_kernel<T, D, MASK, false>), dim3(static_cast<unsigned>(n_dq)),
+                       dim3(kBwdThreads), 0, stream, p, n_qblk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 

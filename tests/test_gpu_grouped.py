@@ -48,6 +48,8 @@ GQA_BWD = [
     (2, 6, 3, 150, 128, "bf16", (30, 0)),
     (1, 4, 4, 96, 64, "f16", (5, 9)),
     (1, 12, 2, 520, 128, "f16", "causal"),
+    (2, 8, 4, 333, 128, "bf16", None),
+    (1, 4, 2, 190, 64, "f16", (40, 3)),
 ]
 
 
