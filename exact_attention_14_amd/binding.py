@@ -430,8 +430,9 @@ def attn_decode(q, k_cache, v_cache, block_table, seq_lens, max_seqlen: int, *, 
     dt = _dtype_code(q)
     if out is None:
         out = torch.empty_like(q)
-    elif tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or not out.is_contiguous():
-        raise ValueError(f"out must be contiguous {q.dtype} {tuple(q.shape)}")
+    elif (tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or not out.is_contiguous()
+          or out.device != q.device):
+        raise ValueError(f"out must be contiguous {q.dtype} {tuple(q.shape)} on {q.device}")
     if lse is None:
         lse = torch.empty((n_seqs, H, n_q), dtype=torch.float32, device=q.device)
     elif (tuple(lse.shape) != (n_seqs, H, n_q) or lse.dtype != torch.float32
@@ -440,6 +441,8 @@ def attn_decode(q, k_cache, v_cache, block_table, seq_lens, max_seqlen: int, *, 
     need = attn_decode_workspace_bytes(q.dtype, n_seqs, H, H_kv, n_q, d, int(max_seqlen))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    elif workspace is not None and (workspace.device != q.device or not workspace.is_contiguous()):
+        raise ValueError(f"workspace must be a contiguous tensor on {q.device}")
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     with torch.cuda.device(q.device):

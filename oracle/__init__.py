@@ -20,17 +20,21 @@ Grouped-query heads and packed variable-length batches (P1 §5's
 extensions) are in ``grouped.py``; decoding over a paged K/V cache in
 ``decode.py``.
 
-Every function here is pinned by ``tests/test_oracle_*.py`` against closed
-forms, invariants, brute force on tiny inputs and an independent library
-routine (torch's CPU float64 scaled-dot-product attention and autograd).
+Every public function here is pinned by ``tests/test_oracle_*.py`` against
+closed forms, invariants, brute force on tiny inputs and an independent
+library routine (torch's CPU float64 scaled-dot-product attention and
+autograd): the definitions (forward_head / forward_rows / forward,
+backward_head, the grouped, packed and paged forms), the mask helpers
+(allowed_matrix against brute-force loops and torch's tril/triu masks,
+allowed_count against its per-mask closed forms) and the pages' online update.
 """
 from .attention import (MASK_MODES, allowed_matrix, allowed_count, forward_head, forward_rows,
-                        forward, backward_head, backward)
+                        forward, backward_head)
 from .decode import forward_decode, gather
 from .grouped import (backward_gqa, backward_varlen, forward_gqa, forward_varlen, group_size)
 from .online import online_forward_head
 
 __all__ = ["MASK_MODES", "allowed_matrix", "allowed_count", "forward_head", "forward_rows",
-           "forward", "backward_head", "backward", "online_forward_head", "group_size",
+           "forward", "backward_head", "online_forward_head", "group_size",
            "forward_gqa", "backward_gqa", "forward_varlen", "backward_varlen", "forward_decode",
            "gather"]

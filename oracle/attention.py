@@ -166,15 +166,3 @@ def backward_head(q, k, v, do, scale: float, mode: str = "none", wl: int = 0, wr
     dS = P * (dP - D[:, None])
     return sigma * (dS @ k), sigma * (dS.T @ q), dv
 
-
-def backward(Q, K, V, dO, scale: float, mode: str = "none", wl: int = 0, wr: int = 0, heads=None):
-    """backward_head over all heads (or the listed (b, h) pairs); unlisted heads stay NaN."""
-    B, H, N, d = Q.shape
-    dQ = np.full((B, H, N, d), np.nan)
-    dK = np.full((B, H, N, d), np.nan)
-    dV = np.full((B, H, N, d), np.nan)
-    todo = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
-    for b, h in todo:
-        dQ[b, h], dK[b, h], dV[b, h] = backward_head(Q[b, h], K[b, h], V[b, h], dO[b, h],
-                                                     scale, mode, wl, wr)
-    return dQ, dK, dV

@@ -4,10 +4,15 @@ Tolerances (against the fp64 oracle):
   O:    max abs error <= 2e-2 and mean abs error <= 2e-3 (fp16/bf16 outputs);
   lse:  max abs error <= 1e-3 (fp32 dot products and one exp2/log2 rounding;
         typically ~1e-5);
-  dQ, dK, dV: relative Frobenius error <= 1e-2 per tensor.
+  dQ, dK, dV: relative Frobenius error <= 1e-2 per tensor, or, where the
+        16-bit roundings the backward must apply (the stored O, from which D
+        is formed, and the products' operands) alone exceed that, 1.5 times
+        the error those roundings give in fp64 (``bwd_rounding``).
 """
 from __future__ import annotations
 
+import concurrent.futures
+import os
 import sys
 
 import numpy as np
@@ -15,6 +20,7 @@ import torch
 
 import oracle
 import exact_attention_14_amd as ea
+from bwd_rounding import grad_bar
 from workloads import draw, to_f64
 
 O_MAX_ABS = 2e-2
@@ -87,8 +93,11 @@ def rel_fro(x: np.ndarray, ref: np.ndarray) -> float:
     return float(np.linalg.norm(x - ref) / max(np.linalg.norm(ref), 1e-30))
 
 
-def bwd_case(B, H, N, d, dtype, mask, seed, scale=None, heads=None, tol=GRAD_REL_FRO):
-    """Forward + backward on the GPU; gradients of the listed heads vs the oracle."""
+def bwd_case(B, H, N, d, dtype, mask, seed, scale=None, heads=None, tol=None):
+    """Forward + backward on the GPU; gradients of the listed heads vs the oracle.
+
+    tol None: each head's bar comes from the rounding model (1e-2 unless its
+    roundings alone exceed that)."""
     scale = (1.0 / np.sqrt(d)) if scale is None else scale
     inp = draw(B, H, N, d, dtype, seed, with_do=True)
     q, k, v, do = (gpu(inp[x]) for x in ("q", "k", "v", "do"))
@@ -99,15 +108,73 @@ def bwd_case(B, H, N, d, dtype, mask, seed, scale=None, heads=None, tol=GRAD_REL
     g = [t.cpu() for t in (dq, dk, dv)]
     todo = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
     worst = [0.0, 0.0, 0.0]
+    bar = 0.0
     for b, h in todo:
         qh, kh, vh, doh = (to_f64(inp[x][b, h]) for x in ("q", "k", "v", "do"))
         ref = oracle.backward_head(qh, kh, vh, doh, scale, name, wl, wr)
+        hb = tol if tol is not None else grad_bar(qh, kh, vh, doh, scale, name, wl, wr, dtype)
+        bar = max(bar, hb)
         for i in range(3):
             gi = to_f64(g[i][b, h])
             assert np.all(np.isfinite(gi))
-            worst[i] = max(worst[i], rel_fro(gi, ref[i]))
+            e = rel_fro(gi, ref[i])
+            worst[i] = max(worst[i], e)
+            assert e <= hb, ("dQ dK dV"[3 * i:3 * i + 2], (b, h), e, hb)
     say(f"  B{B}H{H}N{N}d{d} {dtype} {mask}: rel fro dQ {worst[0]:.3e} dK {worst[1]:.3e} "
-        f"dV {worst[2]:.3e}")
-    for i in range(3):
-        assert worst[i] <= tol, ("dQ dK dV"[3 * i:3 * i + 2], worst[i])
+        f"dV {worst[2]:.3e} (bar {bar:.3e})")
     return worst, (q, k, v, o, lse, do, dq, dk, dv)
+
+
+def oracle_threads() -> int:
+    """Worker threads for oracle sweeps over many heads (numpy releases the GIL
+    in its matrix products and ufuncs); at most 16, the host share of one GPU."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def map_heads(fn, items):
+    """fn over items in parallel threads, one BLAS thread each; results in order."""
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(1), concurrent.futures.ThreadPoolExecutor(oracle_threads()) as ex:
+        return list(ex.map(fn, items))
+
+
+def fwd_all_heads(inp, o_gpu, lse_gpu, scale, mode, wl, wr, row_block=0, heads=None, label=""):
+    """Compare the GPU's O and lse with the oracle over every head (or the listed
+    (b, h) pairs), each head's oracle run in a worker thread.
+
+    Asserts the bars over the whole compared tensor: O max abs and the mean abs
+    over all of its B*H*N*d elements, lse max abs.  Returns (O max abs, O mean
+    abs, lse max abs).
+    """
+    B, H, N, d = inp["q"].shape
+    todo = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    rb = row_block if row_block > 0 else N
+
+    def one(bh):
+        b, h = bh
+        q, k, v = (to_f64(inp[x][b, h]) for x in ("q", "k", "v"))
+        og = to_f64(o_gpu[b, h])
+        lg = lse_gpu[b, h].double().numpy()
+        emax = esum = lmax = 0.0
+        finite = bool(np.all(np.isfinite(og)) and np.all(np.isfinite(lg)))
+        for r0 in range(0, N, rb):
+            rows = np.arange(r0, min(N, r0 + rb))
+            o_ref, l_ref = oracle.forward_rows(rows, q, k, v, scale, mode, wl, wr)
+            e = np.abs(og[rows] - o_ref)
+            emax = max(emax, float(e.max()))
+            esum += float(e.sum())
+            lmax = max(lmax, float(np.abs(lg[rows] - l_ref).max()))
+        return emax, esum, lmax, finite
+
+    res = map_heads(one, todo)
+    mx = max(r[0] for r in res)
+    mean = sum(r[1] for r in res) / (len(todo) * N * d)
+    lmx = max(r[2] for r in res)
+    worst_head = todo[int(np.argmax([r[0] for r in res]))]
+    say(f"  {label} {len(todo)} heads: O max abs {mx:.3e} (head {worst_head}) mean abs "
+        f"{mean:.3e} over {len(todo) * N * d} elements; lse max abs {lmx:.3e}")
+    assert all(r[3] for r in res), (label, "non-finite output")
+    assert mx <= O_MAX_ABS, (label, mx)
+    assert mean <= O_MEAN_ABS, (label, mean)
+    assert lmx <= LSE_MAX_ABS, (label, lmx)
+    return mx, mean, lmx

@@ -19,12 +19,11 @@ pytestmark = pytest.mark.gpu
 def test_backward_ragged(N, d, dtype):
     # With only one or two allowed keys per row, dP - D nearly cancels and the
     # rounding of O to bf16 (D is formed from the stored O) dominates dS: the
-    # same roundings applied in fp64 give 6.6e-2 for N = 2 causal.  That case
-    # gets a 1e-1 bar; every other case keeps 1e-2.
-    tol = 1e-1 if (dtype == "bf16" and N < 16) else 1e-2
+    # same roundings applied in fp64 give ~7e-2 for N = 2 causal at d = 64.
+    # Each head's bar is 1e-2, or 1.5x that modelled error where it is larger.
     for mask in [None, "causal", (9, 4)]:
         say(f"bwd N={N} d={d} {dtype} mask={mask}")
-        bwd_case(1, 2, N, d, dtype, mask, seed=N + d, tol=tol)
+        bwd_case(1, 2, N, d, dtype, mask, seed=N + d)
 
 
 @pytest.mark.parametrize("mask", [None, "causal", (1, 0), (100, 0), (63, 65), (2000, 2000)])

@@ -77,3 +77,25 @@ def test_decode_matches_the_forward_on_the_last_rows():
     say(f"  decode vs forward rows: max abs {diff:.3e}")
     assert diff <= 2e-2
     assert (l_f[0, :, N - 3:] - l_d[0]).abs().max().item() <= 1e-3
+
+
+def test_decode_binding_rejects_misplaced_buffers():
+    """The binding checks a caller's workspace and output buffers like the other
+    entry points do: on the query's device and contiguous, else ValueError
+    before the library is called."""
+    lens = [300, 8192]
+    inp = draw_paged(lens, 32, 1, 1, 128, "f16", 128, seed=3)
+    args = [gpu(inp[x]) for x in ("q", "k", "v", "block_table", "seq_lens")]
+    need = ea.attn_decode_workspace_bytes(torch.float16, 2, 32, 1, 1, 128, max(lens))
+    assert need > 0
+    with pytest.raises(ValueError):
+        ea.attn_decode(*args, max(lens), workspace=torch.empty(need, dtype=torch.uint8))
+    strided = torch.empty(2 * need, dtype=torch.uint8, device="cuda")[::2]
+    with pytest.raises(ValueError):
+        ea.attn_decode(*args, max(lens), workspace=strided)
+    with pytest.raises(ValueError):
+        ea.attn_decode(*args, max(lens), out=torch.empty_like(inp["q"]))
+    ok = torch.empty(need, dtype=torch.uint8, device="cuda")
+    o, lse = ea.attn_decode(*args, max(lens), workspace=ok)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all())

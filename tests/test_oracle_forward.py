@@ -216,3 +216,59 @@ def test_invalid_mask_arguments_are_rejected():
         oracle.forward_head(q, k, v, 1.0, "sliding", -1, 0)
     with pytest.raises(ValueError):
         oracle.forward_head(q, k, v, 1.0, "diagonal")
+
+
+# ------------------------------------------------------------ allowed counts
+@pytest.mark.parametrize("N", [1, 2, 7, 64, 65, 300])
+@pytest.mark.parametrize("mode,wl,wr", MASKS + [("sliding", 400, 400), ("sliding", 64, 0)])
+def test_allowed_count_closed_forms(N, mode, wl, wr):
+    """#A_i from oracle.allowed_count equals the count written out per mask
+    rule: N without a mask, i + 1 under causal, min(i, wl) + 1 + min(N-1-i, wr)
+    for a sliding window (P4 "usage" variants, both window ends inclusive)."""
+    got = oracle.allowed_count(N, mode, wl, wr)
+    want = np.array([count_allowed(i, N, mode, wl, wr) for i in range(N)])
+    assert got.shape == (N,)
+    assert np.array_equal(got, want)
+
+
+def test_allowed_count_catches_a_transposed_sum():
+    """Planted mistake: counting per key (columns) instead of per query row.
+    Causal column counts are N - j, not i + 1, so the closed form rejects it;
+    an asymmetric sliding window is caught the same way."""
+    for N, mode, wl, wr in [(50, "causal", 0, 0), (40, "sliding", 5, 1)]:
+        r = np.arange(N)
+        wrong = oracle.allowed_matrix(r, r, N, mode, wl, wr).sum(axis=0)
+        want = np.array([count_allowed(i, N, mode, wl, wr) for i in range(N)])
+        assert not np.array_equal(wrong, want)
+        assert np.array_equal(oracle.allowed_count(N, mode, wl, wr), want)
+
+
+@pytest.mark.parametrize("mode,wl,wr", [("none", 0, 0), ("causal", 0, 0), ("sliding", 6, 3)])
+def test_multi_head_forward_matches_torch_sdpa(mode, wl, wr):
+    """The [B, H, N, d] wrapper (every head, and a listed subset) against
+    torch's float64 SDPA over the whole batch at once, with its lse from
+    torch.logsumexp: a head written to the wrong (b, h) slot or a subset that
+    leaks into unlisted heads fails here."""
+    B, H, N, d = 2, 3, 70, 16
+    t = draw(B, H, N, d, "bf16", 31)
+    Q, K, V = (to_f64(t[x]) for x in ("q", "k", "v"))
+    scale = 0.3
+    sig = float(np.float32(scale))
+    tq, tk, tv = (torch.from_numpy(x) for x in (Q, K, V))
+    msk = torch_mask(N, mode, wl, wr)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=msk, scale=sig)
+    s = sig * (tq @ tk.transpose(-1, -2))
+    if msk is not None:
+        s = s.masked_fill(~msk, float("-inf"))
+    lref = torch.logsumexp(s, dim=-1).numpy()
+    O, L = oracle.forward(Q, K, V, scale, mode, wl, wr)
+    np.testing.assert_allclose(O, ref.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(L, lref, rtol=0, atol=1e-12)
+    O2, L2 = oracle.forward(Q, K, V, scale, mode, wl, wr, heads=[(1, 2), (0, 1)])
+    for b in range(B):
+        for h in range(H):
+            if (b, h) in [(1, 2), (0, 1)]:
+                np.testing.assert_array_equal(O2[b, h], O[b, h])
+                np.testing.assert_array_equal(L2[b, h], L[b, h])
+            else:
+                assert np.all(np.isnan(O2[b, h])) and np.all(np.isnan(L2[b, h]))
