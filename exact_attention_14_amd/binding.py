@@ -21,14 +21,18 @@ ATTN_F16, ATTN_BF16 = 0, 1
 ATTN_MASK_NONE, ATTN_MASK_CAUSAL, ATTN_MASK_SLIDING = 0, 1, 2
 STATUS = {0: "ATTN_OK", 1: "ATTN_E_NULLPTR", 2: "ATTN_E_SHAPE", 3: "ATTN_E_UNSUPPORTED",
           4: "ATTN_E_MASK", 5: "ATTN_E_SCALE", 6: "ATTN_E_ALIGN", 7: "ATTN_E_ALIAS",
-          8: "ATTN_E_WORKSPACE", 9: "ATTN_E_HIP"}
+          8: "ATTN_E_WORKSPACE", 9: "ATTN_E_HIP", 10: "ATTN_E_SCRATCH"}
+
+# Fixed device scratch of attn_bwd_noalloc per GPU (ATTN_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 # Every symbol include/attn.h declares.
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str",
            "attn_fwd_check", "attn_bwd_check", "attn_fwd_tiles", "attn_kv_tile_range",
            "attn_fwd_workgroup", "attn_bwd_kv_workgroup", "attn_fwd_gqa", "attn_bwd_gqa",
            "attn_fwd_varlen", "attn_bwd_varlen", "attn_bwd_gqa_workspace_bytes",
-           "attn_bwd_varlen_workspace_bytes", "attn_decode", "attn_decode_workspace_bytes")
+           "attn_bwd_varlen_workspace_bytes", "attn_decode", "attn_decode_workspace_bytes",
+           "attn_bwd_noalloc")
 
 
 class AttnError(RuntimeError):
@@ -56,6 +60,9 @@ def lib() -> ctypes.CDLL:
     L.attn_bwd.restype = i32
     L.attn_bwd_check.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64,
                                  i64, f32, i32, i64, i64]
+    L.attn_bwd_noalloc.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                   f32, i32, i64, i64, vp]
+    L.attn_bwd_noalloc.restype = i32
     L.attn_bwd_check.restype = i32
     L.attn_fwd_gqa.argtypes = [i32, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32, i64, i64,
                                vp]
@@ -267,6 +274,34 @@ def attn_bwd(q, k, v, o, lse, do, *, mask=None, scale=None, workspace=None):
                                     dv.data_ptr(), workspace.data_ptr(), ws_bytes, B, H, H_kv, N,
                                     d, float(scale), mode, wl, wr, _stream_ptr(q.device))
     _raise(fn, st)
+    return dq, dk, dv
+
+
+def attn_bwd_noalloc(q, k, v, o, lse, do, *, out=None, mask=None, scale=None):
+    """attn_bwd through the library's allocation-free entry point (fixed per-GPU
+    scratch; standard multi-head attention, H_kv = H).  ``out`` may hold
+    caller-allocated (dQ, dK, dV) tensors, so that a call allocates nothing."""
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", do)):
+        _check4(name, t, q)
+    _check_gpu(q)
+    _check_lse(lse, q)
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    mode, wl, wr = mask_args(mask)
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    for name, t in zip(("dq", "dk", "dv"), out):
+        _check4(name, t, q)
+    dq, dk, dv = out
+    with torch.cuda.device(q.device):
+        st = lib().attn_bwd_noalloc(_dtype_code(q), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                    o.data_ptr(), lse.data_ptr(), do.data_ptr(), dq.data_ptr(),
+                                    dk.data_ptr(), dv.data_ptr(), B, H, N, d, float(scale), mode,
+                                    wl, wr, _stream_ptr(q.device))
+    _raise("attn_bwd_noalloc", st)
     return dq, dk, dv
 
 

@@ -5,14 +5,39 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "attn.h"
 #include "kernels.hpp"
 #include "plan.hpp"
 #include "validate.hpp"
 
+// Workspace of attn_bwd_noalloc: a fixed array in the code object, one copy
+// per GPU.  In host code this name is only a handle for hipGetSymbolAddress,
+// never a device address; kernels get the per-device address it returns.
+static __device__ __align__(256) char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
 namespace attn {
 namespace {
+
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_addr[kMaxDevices];  // device address of `scratch` on each device, once known
+
+// The current device's copy of `scratch`, looked up once per device.
+attn_status scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_E_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return ATTN_E_HIP;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return ATTN_OK;
+}
 
 // Scores enter the exp2 domain as s * c with c = |scale| * log2(e) > 0; a
 // negative scale is folded into Q by flipping its sign bits.  A zero scale
@@ -137,6 +162,24 @@ attn_status attn_bwd(attn_dtype dt, const void* Q, const void* K, const void* V,
   return attn::bwd_impl(dt, Q, K, V, O, lse, dO, dQ, dK, dV, workspace, workspace_bytes, nullptr,
                         attn::fixed_geometry(B, H, H, N, d), scale, mode, window_left,
                         window_right, stream);
+}
+
+attn_status attn_bwd_noalloc(attn_dtype dt, const void* Q, const void* K, const void* V,
+                             const void* O, const float* lse, const void* dO, void* dQ, void* dK,
+                             void* dV, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                             attn_mask_mode mode, int64_t window_left, int64_t window_right,
+                             void* stream) {
+  const attn::Geometry g = attn::fixed_geometry(B, H, H, N, d);
+  // Every argument but the workspace first, before any HIP call.
+  attn_status s = attn::bwd_check_g(dt, Q, K, V, O, lse, dO, dQ, dK, dV, nullptr, 0, nullptr, g,
+                                    scale, mode, window_left, window_right, false);
+  if (s != ATTN_OK) return s;
+  if (attn::bwd_workspace_bytes(g) > ATTN_NOALLOC_SCRATCH_BYTES) return ATTN_E_SCRATCH;
+  void* ws = nullptr;
+  s = attn::scratch_address(&ws);
+  if (s != ATTN_OK) return s;
+  return attn::bwd_impl(dt, Q, K, V, O, lse, dO, dQ, dK, dV, ws, ATTN_NOALLOC_SCRATCH_BYTES,
+                        nullptr, g, scale, mode, window_left, window_right, stream);
 }
 
 attn_status attn_bwd_gqa(attn_dtype dt, const void* Q, const void* K, const void* V,

@@ -177,7 +177,7 @@ attn_status bwd_check_g(int dt, const void* Q, const void* K, const void* V, con
                         const float* lse, const void* dO, const void* dQ, const void* dK,
                         const void* dV, const void* ws, size_t ws_bytes,
                         const int32_t* cu_seqlens, const Geometry& g, float scale, int mode,
-                        int64_t wl, int64_t wr) {
+                        int64_t wl, int64_t wr, bool check_ws) {
   attn_status s = check_geometry(dt, g);
   if (s != ATTN_OK) return s;
   const Sizes z = sizes_of(g);
@@ -189,14 +189,14 @@ attn_status bwd_check_g(int dt, const void* Q, const void* K, const void* V, con
   a.in_bytes[1] = a.in_bytes[2] = z.kv;
   a.in_bytes[4] = z.rows;
   add_offsets(a, cu_seqlens);
-  a.n_out = 4;
+  a.n_out = check_ws ? 4 : 3;
   a.out[0] = dQ; a.out[1] = dK; a.out[2] = dV; a.out[3] = ws;
   a.out_bytes[0] = z.q;
   a.out_bytes[1] = a.out_bytes[2] = z.kv;
   a.out_bytes[3] = wb;
   s = check_common(a);
   if (s != ATTN_OK) return s;
-  if (ws_bytes < wb) return ATTN_E_WORKSPACE;
+  if (check_ws && ws_bytes < wb) return ATTN_E_WORKSPACE;
   return ATTN_OK;
 }
 
@@ -304,6 +304,8 @@ const char* attn_status_str(attn_status s) {
     case ATTN_E_ALIGN: return "a device pointer is not 16-byte aligned";
     case ATTN_E_ALIAS: return "an output overlaps an input or another output";
     case ATTN_E_WORKSPACE: return "workspace missing or too small";
+    case ATTN_E_SCRATCH:
+      return "the sizes need more scratch than the allocation-free entry point holds";
     case ATTN_E_HIP: return "HIP runtime error at launch";
   }
   return "unknown status";

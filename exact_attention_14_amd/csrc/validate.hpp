@@ -74,7 +74,7 @@ attn_status bwd_check_g(int dt, const void* Q, const void* K, const void* V, con
                         const float* lse, const void* dO, const void* dQ, const void* dK,
                         const void* dV, const void* ws, size_t ws_bytes,
                         const int32_t* cu_seqlens, const Geometry& g, float scale, int mode,
-                        int64_t wl, int64_t wr);
+                        int64_t wl, int64_t wr, bool check_ws = true);
 
 // Split-KV decoding over a paged cache (decode.hpp): validation, and the
 // workspace (fp32 partial O and lse per split) it needs.

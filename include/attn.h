@@ -86,7 +86,8 @@ typedef enum attn_status {
   ATTN_E_ALIGN = 6,       /* a device pointer is not 16-byte aligned */
   ATTN_E_ALIAS = 7,       /* an output overlaps an input or another output */
   ATTN_E_WORKSPACE = 8,   /* workspace missing or smaller than required */
-  ATTN_E_HIP = 9          /* the HIP runtime reported an error at launch */
+  ATTN_E_HIP = 9,         /* the HIP runtime reported an error at launch */
+  ATTN_E_SCRATCH = 10     /* attn_bwd_noalloc: the sizes need more than its fixed scratch */
 } attn_status;
 
 /*
@@ -105,6 +106,9 @@ attn_status attn_fwd(attn_dtype dt, const void* Q, const void* K, const void* V,
                      float* lse, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
                      attn_mask_mode mode, int64_t window_left, int64_t window_right,
                      void* stream);
+
+/* Size of the fixed device scratch of attn_bwd_noalloc, per GPU. */
+#define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 
 /*
  * attn_bwd_workspace_bytes -- size in bytes of the device workspace attn_bwd
@@ -172,6 +176,31 @@ attn_status attn_fwd_gqa(attn_dtype dt, const void* Q, const void* K, const void
                          float* lse, int64_t B, int64_t H, int64_t H_kv, int64_t N, int64_t d,
                          float scale, attn_mask_mode mode, int64_t window_left,
                          int64_t window_right, void* stream);
+
+/*
+ * attn_bwd_noalloc -- attn_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, serving loops, harnesses that forbid
+ * hipMalloc): the same computation with the same kernels, but the workspace
+ * is a fixed array of ATTN_NOALLOC_SCRATCH_BYTES inside the library's code
+ * object, one per GPU, which the library holds until the process ends.
+ *
+ *   Arguments as for attn_bwd, without workspace and workspace_bytes; every
+ *   buffer still belongs to the caller and to the current device.
+ * Validates every argument like attn_bwd, then returns ATTN_E_SCRATCH without
+ * launching anything if attn_bwd_workspace_bytes(dt, B, H, N, d) exceeds
+ * ATTN_NOALLOC_SCRATCH_BYTES (two float32 values per row: up to 4,194,240
+ * rows B*H*N).  Calls no allocating routine; the first call on a device looks
+ * up that device's copy of the array (hipGetSymbolAddress), later calls reuse
+ * the address.  The array needs no clearing: every value the second kernel
+ * reads is written by the first kernel of the same call.  All calls on one GPU
+ * share its array, so calls that overlap on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller.
+ */
+attn_status attn_bwd_noalloc(attn_dtype dt, const void* Q, const void* K, const void* V,
+                             const void* O, const float* lse, const void* dO, void* dQ, void* dK,
+                             void* dV, int64_t B, int64_t H, int64_t N, int64_t d, float scale,
+                             attn_mask_mode mode, int64_t window_left, int64_t window_right,
+                             void* stream);
 
 /*
  * attn_bwd_gqa -- attn_bwd with K, V, dK, dV of shape [B, H_kv, N, d]:

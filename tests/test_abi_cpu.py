@@ -26,7 +26,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     lib = ea.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -34,8 +34,9 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for s in range(10):
+    for s in range(11):
         assert ea.attn_status_str(s)
+    assert "scratch" in ea.attn_status_str(10)
 
 
 def test_launching_entry_points_reject_bad_arguments_before_any_hip_call():
@@ -291,3 +292,34 @@ def test_binding_rejects_host_tensors_before_any_library_call():
         ea.attn_bwd(q, q, q, q, lse, q)
     with pytest.raises(ValueError, match="shape"):
         ea.attn_bwd(q, q[:, :, :4], q, q, lse, q)
+
+
+def test_noalloc_backward_validates_before_any_hip_call():
+    """attn_bwd_noalloc checks every argument like attn_bwd, and sizes whose
+    workspace exceeds its fixed scratch fail with ATTN_E_SCRATCH, all before
+    any HIP call and without touching the buffers."""
+    lib = ea.lib()
+    buf = ctypes.create_string_buffer(1 << 16)
+    base = (ctypes.addressof(buf) + 255) // 256 * 256
+    Q, K, V, O, L, dO = (base + 4096 * i for i in range(6))
+    dQ, dK, dV = (base + 4096 * i for i in range(6, 9))
+    ok = [0, Q, K, V, O, L, dO, dQ, dK, dV, 1, 1, 8, 64, 0.1, 1, 0, 0, None]
+    bad = list(ok)
+    bad[1] = None
+    assert lib.attn_bwd_noalloc(*bad) == 1            # NULL input
+    bad = list(ok)
+    bad[7] = Q + 16
+    assert lib.attn_bwd_noalloc(*bad) == 7            # dQ overlaps Q
+    bad = list(ok)
+    bad[13] = 96
+    assert lib.attn_bwd_noalloc(*bad) == 3            # unsupported d
+    assert bytes(buf) == b"\0" * len(buf)
+    # Sizes beyond the scratch: addresses far apart so nothing overlaps (never dereferenced).
+    big = [0] + [(i + 1) << 40 for i in range(9)] + [1, 1, 5_000_000, 64, 0.1, 0, 0, 0, None]
+    need = ea.attn_bwd_workspace_bytes(__import__("torch").float16, 1, 1, 5_000_000, 64)
+    assert need > binding.NOALLOC_SCRATCH_BYTES
+    assert lib.attn_bwd_noalloc(*big) == 10
+    # the largest row count that fits: two 256-byte-padded float32 arrays
+    rows = binding.NOALLOC_SCRATCH_BYTES // 8 // 64 * 64
+    assert ea.attn_bwd_workspace_bytes(__import__("torch").float16, 1, 1, rows, 64) <= \
+        binding.NOALLOC_SCRATCH_BYTES
