@@ -32,7 +32,7 @@ EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_status_str"
            "attn_fwd_workgroup", "attn_bwd_kv_workgroup", "attn_fwd_gqa", "attn_bwd_gqa",
            "attn_fwd_varlen", "attn_bwd_varlen", "attn_bwd_gqa_workspace_bytes",
            "attn_bwd_varlen_workspace_bytes", "attn_decode", "attn_decode_workspace_bytes",
-           "attn_bwd_noalloc")
+           "attn_bwd_noalloc", "attn_fwd_persistent")
 
 
 class AttnError(RuntimeError):
@@ -67,6 +67,9 @@ def lib() -> ctypes.CDLL:
     L.attn_fwd_gqa.argtypes = [i32, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32, i64, i64,
                                vp]
     L.attn_fwd_gqa.restype = i32
+    L.attn_fwd_persistent.argtypes = [i32, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, f32, i32,
+                                      i64, i64, vp]
+    L.attn_fwd_persistent.restype = i32
     L.attn_bwd_gqa.argtypes = [i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i64, i64, i64, i64,
                                i64, f32, i32, i64, i64, vp]
     L.attn_bwd_gqa.restype = i32
@@ -170,13 +173,15 @@ def _check_lse(lse: torch.Tensor, q: torch.Tensor):
 
 
 def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, mask=None, scale=None,
-             out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+             out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+             persistent: bool = False):
     """Forward pass; returns (O, lse).  Inputs: contiguous q [B, H, N, d] and k, v
     [B, H_kv, N, d] on a GPU (H_kv < H: grouped-query attention, query head h
     reads key/value head h // (H // H_kv)).
 
     ``scale`` defaults to 1/sqrt(d) (P1 §1).  ``out``/``lse`` may be given to
-    write into preallocated buffers.
+    write into preallocated buffers.  ``persistent`` selects the library's
+    persistent-scheduling entry point (attn_fwd_persistent; same results).
     """
     if q.dim() != 4 or k.dim() != 4:
         raise ValueError("q must be [B, H, N, d] and k [B, H_kv, N, d]")
@@ -200,7 +205,12 @@ def attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, *, mask=None, sc
         _check_lse(lse, q)
     # The library launches on the calling thread's current device.
     with torch.cuda.device(q.device):
-        if H_kv == H:
+        if persistent:
+            fn = "attn_fwd_persistent"
+            st = lib().attn_fwd_persistent(dt, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                           out.data_ptr(), lse.data_ptr(), B, H, H_kv, N, d,
+                                           float(scale), mode, wl, wr, _stream_ptr(q.device))
+        elif H_kv == H:
             fn = "attn_fwd"
             st = lib().attn_fwd(dt, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                 lse.data_ptr(), B, H, N, d, float(scale), mode, wl, wr,

@@ -69,6 +69,53 @@ namespace {
 
 constexpr float kSumBound = 256.0f;  // 2^kTau, kTau = 8
 
+// Work queues of the persistent forward (fwd_kernel with PERSIST): the next unclaimed
+// slot of each die's run of work items, and the number of workgroups that
+// found every queue empty.  Zero when the code object loads; the last
+// workgroup of every persistent launch sets them back to zero, so a launch
+// needs no clearing beforehand (and two persistent launches must not run at
+// the same time on one device).
+__device__ uint32_t fwd_queue_next[kNumXcd];
+__device__ uint32_t fwd_queue_done;
+
+// A work item for a persistent workgroup (see fwd_kernel), as the id of the
+// ordered launch's workgroup that would run it, or -1 when none is left
+// (thread 0 only; vector atomics).
+__device__ __forceinline__ int claim_item(uint32_t n_wg) {
+  const uint32_t x0 = blockIdx.x % kNumXcd;
+  int v = -1;
+  for (uint32_t k = 0; k < kNumXcd && v < 0; ++k) {
+    const uint32_t x = (x0 + k) % kNumXcd;
+    // slots of die x: the ordered launch's workgroups w < n_wg with w % kNumXcd == x
+    const uint32_t count = (n_wg + kNumXcd - 1 - x) / kNumXcd;
+    const uint32_t slot = __hip_atomic_fetch_add(&fwd_queue_next[x], 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    if (slot < count) v = static_cast<int>(slot * kNumXcd + x);
+  }
+  if (v < 0) {
+    // Every queue is empty: the last workgroup to see it resets them.
+    const uint32_t d = __hip_atomic_fetch_add(&fwd_queue_done, 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    if (d == gridDim.x - 1) {
+      for (uint32_t x = 0; x < kNumXcd; ++x)
+        __hip_atomic_store(&fwd_queue_next[x], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&fwd_queue_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  return v;
+}
+
+// Thread 0's claimed item passed on to the whole workgroup through LDS; the
+// barriers also keep the next item's loads from overwriting LDS stages that
+// the last item's wavefronts still read.
+__device__ __forceinline__ int share_item(int v, int* slot_lds) {
+  if (threadIdx.x == 0) *slot_lds = v;
+  __syncthreads();
+  const int w = *slot_lds;
+  __syncthreads();
+  return w;
+}
+
 template <int D, int NWAVES>
 struct FwdLayout {
   static constexpr int BC = kFwdBlockK;
@@ -95,9 +142,18 @@ struct FwdLayout {
 // halves visit the same key tiles, so every K/V tile brought into LDS serves
 // 256 rows, as in the unmasked kernel, without the uneven tile counts that
 // 256 consecutive rows have under a causal or sliding mask.
-template <typename T, int D, int MASK, bool PAIR>
+//
+// PERSIST: the grid holds only as many workgroups as the chip runs at once;
+// each claims work items from a queue per die (claim_item) until all are
+// done.  A claimed slot s of die x is the item that workgroup s * kNumXcd + x
+// runs in the ordered launch, so items keep their die and their
+// heaviest-first order within it; a workgroup whose own die has run out takes
+// items from the other dies' queues.  In the ordered launch the hardware
+// dispatcher hands out the same workgroups, in id order, as compute-unit
+// slots free up.
+template <typename T, int D, int MASK, bool PAIR, bool PERSIST>
 __global__ __launch_bounds__(64 * (PAIR ? 8 : fwd_waves(MASK))) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void fwd_kernel(FwdParams p) {
+void fwd_kernel(FwdParams p, uint32_t n_wg) {
   constexpr int NWAVES = PAIR ? 8 : fwd_waves(MASK);
   using L = FwdLayout<D, NWAVES>;
   constexpr int BR = fwd_block_q(MASK), BC = kFwdBlockK;
@@ -108,6 +164,7 @@ void fwd_kernel(FwdParams p) {
 
   __shared__ __attribute__((aligned(16))) char k_lds0[L::K_BYTES], k_lds1[L::K_BYTES];
   __shared__ __attribute__((aligned(16))) char v_lds0[L::V_BYTES], v_lds1[L::V_BYTES];
+  __shared__ int slot_lds;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, half = lane >> 5, r32 = lane & 31;
@@ -116,12 +173,19 @@ void fwd_kernel(FwdParams p) {
   // at 32 * (wave % 4) within the block.
   const int sub = PAIR ? wave / 4 : 0, wrow = PAIR ? wave % 4 : wave;
 
+  // A persistent workgroup claims its next item only when it has finished
+  // the current one: claiming one ahead (so that the atomic's round trip
+  // overlaps the work) measured 3-9% slower, since an item reserved early is
+  // no longer available to a workgroup that frees up sooner.
+  for (int wg = PERSIST ? share_item(threadIdx.x == 0 ? claim_item(n_wg) : -1, &slot_lds)
+                        : static_cast<int>(blockIdx.x);
+       wg >= 0; wg = PERSIST ? share_item(threadIdx.x == 0 ? claim_item(n_wg) : -1, &slot_lds) : -1) {
   int64_t head, qblk;
   const int hdiv = PAIR ? 2 : 1;
   if (p.g.cu_seqlens == nullptr)
-    fwd_item(blockIdx.x, p.n_heads / hdiv, p.n_qblk, MASK, &head, &qblk);
+    fwd_item(wg, p.n_heads / hdiv, p.n_qblk, MASK, &head, &qblk);
   else
-    packed_item(blockIdx.x, p.g.H / hdiv, p.n_heads / p.g.H, p.n_qblk, false, &head, &qblk);
+    packed_item(wg, p.g.H / hdiv, p.n_heads / p.g.H, p.n_qblk, false, &head, &qblk);
   if (PAIR) {
     // item (outer, pair) -> query head outer*H + 2*pair + sub
     const int64_t hp = p.g.H / 2;
@@ -133,7 +197,7 @@ void fwd_kernel(FwdParams p) {
   const HeadRows hr = query_rows(p.g, head);
   const int N = static_cast<int>(hr.len);
   const int q0 = static_cast<int>(qblk) * BR;
-  if (q0 >= N) return;
+  if (q0 >= N) continue;
   const size_t qoff = static_cast<size_t>(hr.q_row0) * ROW_BYTES;
   const size_t kvoff = static_cast<size_t>(hr.kv_row0) * ROW_BYTES;
   const uint32_t head_bytes = static_cast<uint32_t>(N) * ROW_BYTES;
@@ -417,43 +481,63 @@ void fwd_kernel(FwdParams p) {
   }
   const auto rL = make_rsrc(p.lse + hr.q_row0, static_cast<uint32_t>(N) * 4);
   buf_store4((m + log2f(lt)) * kLn2, rL, static_cast<uint32_t>(qrow) * 4);
+  }
+}
+
+// A persistent launch runs as many workgroups as the chip holds at once: two
+// wavefronts per SIMD, four SIMDs per compute unit.
+unsigned persistent_grid(int64_t n_wg, int waves, int n_cu) {
+  const int64_t resident = static_cast<int64_t>(n_cu) * (8 / waves);
+  return static_cast<unsigned>(n_wg < resident ? n_wg : resident);
 }
 
 template <typename T, int D, int MASK>
-hipError_t launch_one(const FwdParams& p, int64_t n_wg, hipStream_t stream) {
+hipError_t launch_one(const FwdParams& p, int64_t n_wg, int persist_cus, hipStream_t stream) {
   // Pairs help fixed-length batches (+3.4% at B4 H32 H_kv8 N4096 causal); a
   // packed batch's many short items run better in four-wavefront workgroups.
   if (MASK != kNone && p.g.group % 2 == 0 && p.g.cu_seqlens == nullptr) {
-    hipLaunchKernelGGL((fwd_kernel<T, D, MASK, true>), dim3(static_cast<unsigned>(n_wg / 2)),
-                       dim3(64 * 8), 0, stream, p);
+    if (persist_cus > 0)
+      hipLaunchKernelGGL((fwd_kernel<T, D, MASK, true, true>),
+                         dim3(persistent_grid(n_wg / 2, 8, persist_cus)), dim3(64 * 8), 0, stream, p,
+                         static_cast<uint32_t>(n_wg / 2));
+    else
+      hipLaunchKernelGGL((fwd_kernel<T, D, MASK, true, false>), dim3(static_cast<unsigned>(n_wg / 2)),
+                         dim3(64 * 8), 0, stream, p, 0u);
   } else {
-    hipLaunchKernelGGL((fwd_kernel<T, D, MASK, false>), dim3(static_cast<unsigned>(n_wg)),
-                       dim3(64 * fwd_waves(MASK)), 0, stream, p);
+    if (persist_cus > 0)
+      hipLaunchKernelGGL((fwd_kernel<T, D, MASK, false, true>),
+                         dim3(persistent_grid(n_wg, fwd_waves(MASK), persist_cus)),
+                         dim3(64 * fwd_waves(MASK)), 0, stream, p, static_cast<uint32_t>(n_wg));
+    else
+      hipLaunchKernelGGL((fwd_kernel<T, D, MASK, false, false>), dim3(static_cast<unsigned>(n_wg)),
+                         dim3(64 * fwd_waves(MASK)), 0, stream, p, 0u);
   }
   return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t launch_mask(const FwdParams& p, int mode, int64_t n_wg, hipStream_t stream) {
+hipError_t launch_mask(const FwdParams& p, int mode, int64_t n_wg, int persist_cus,
+                       hipStream_t stream) {
   switch (mode) {
-    case kCausal: return launch_one<T, D, kCausal>(p, n_wg, stream);
-    case kSliding: return launch_one<T, D, kSliding>(p, n_wg, stream);
-    default: return launch_one<T, D, kNone>(p, n_wg, stream);
+    case kCausal: return launch_one<T, D, kCausal>(p, n_wg, persist_cus, stream);
+    case kSliding: return launch_one<T, D, kSliding>(p, n_wg, persist_cus, stream);
+    default: return launch_one<T, D, kNone>(p, n_wg, persist_cus, stream);
   }
 }
 
 template <typename T>
-hipError_t launch_d(const FwdParams& p, int d, int mode, int64_t n_wg, hipStream_t stream) {
-  return d == 64 ? launch_mask<T, 64>(p, mode, n_wg, stream)
-                 : launch_mask<T, 128>(p, mode, n_wg, stream);
+hipError_t launch_d(const FwdParams& p, int d, int mode, int64_t n_wg, int persist_cus,
+                    hipStream_t stream) {
+  return d == 64 ? launch_mask<T, 64>(p, mode, n_wg, persist_cus, stream)
+                 : launch_mask<T, 128>(p, mode, n_wg, persist_cus, stream);
 }
 
 }  // namespace
 
 hipError_t launch_fwd(const FwdParams& p, int dt_bf16, int d, int mode, int64_t n_wg,
-                      hipStream_t stream) {
-  return dt_bf16 ? launch_d<__bf16>(p, d, mode, n_wg, stream)
-                 : launch_d<_Float16>(p, d, mode, n_wg, stream);
+                      int persist_cus, hipStream_t stream) {
+  return dt_bf16 ? launch_d<__bf16>(p, d, mode, n_wg, persist_cus, stream)
+                 : launch_d<_Float16>(p, d, mode, n_wg, persist_cus, stream);
 }
 
 }  // namespace attn

@@ -58,8 +58,9 @@ struct BwdParams {
   float lse_mul;  // -log2(e) / c: exp2(c * (s + lse * lse_mul)) = exp(scale * q.k - lse)
 };
 
+// persist_cus > 0: persistent launch on a device with that many compute units.
 hipError_t launch_fwd(const FwdParams& p, int dt_bf16, int d, int mode, int64_t n_wg,
-                      hipStream_t stream);
+                      int persist_cus, hipStream_t stream);
 hipError_t launch_bwd(const BwdParams& p, int dt_bf16, int d, int mode, hipStream_t stream);
 hipError_t launch_decode(const DecParams& p, int dt_bf16, int d, int mode, hipStream_t stream);
 

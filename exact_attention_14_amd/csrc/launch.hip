@@ -63,11 +63,36 @@ HeadGeom head_geom(const Geometry& g, const int32_t* cu_seqlens) {
 // Windows are read only for a sliding mask and act as unbounded from the
 // head's row count on (for a packed batch, from T on: every sequence is
 // shorter).
+// Compute units of the current device, looked up once per device.
+std::mutex g_cu_mu;
+int g_cu_count[kMaxDevices];
+
+attn_status compute_units(int* out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ATTN_E_HIP;
+  std::lock_guard<std::mutex> lock(g_cu_mu);
+  if (g_cu_count[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      return ATTN_E_HIP;
+    g_cu_count[dev] = n;
+  }
+  *out = g_cu_count[dev];
+  return ATTN_OK;
+}
+
 attn_status fwd_impl(attn_dtype dt, const void* Q, const void* K, const void* V, void* O,
                      float* lse, const int32_t* cu_seqlens, const Geometry& g, float scale,
-                     attn_mask_mode mode, int64_t wl, int64_t wr, void* stream) {
+                     attn_mask_mode mode, int64_t wl, int64_t wr, void* stream,
+                     bool persistent = false) {
   attn_status s = fwd_check_g(dt, Q, K, V, O, lse, cu_seqlens, g, scale, mode, wl, wr);
   if (s != ATTN_OK) return s;
+  int n_cu = 0;
+  if (persistent) {
+    s = compute_units(&n_cu);
+    if (s != ATTN_OK) return s;
+  }
   FwdParams p{};
   p.Q = Q; p.K = K; p.V = V; p.O = O; p.lse = lse;
   p.g = head_geom(g, cu_seqlens);
@@ -78,7 +103,7 @@ attn_status fwd_impl(attn_dtype dt, const void* Q, const void* K, const void* V,
   p.c = exp2_coeff(scale);
   p.qsign = scale < 0.0f ? 0x80008000u : 0u;
   const int64_t n_wg = g.n_heads() * p.n_qblk;
-  hipError_t e = launch_fwd(p, dt == ATTN_BF16, static_cast<int>(g.d), mode, n_wg,
+  hipError_t e = launch_fwd(p, dt == ATTN_BF16, static_cast<int>(g.d), mode, n_wg, n_cu,
                             static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ATTN_OK : ATTN_E_HIP;
 }
@@ -142,6 +167,14 @@ attn_status attn_fwd_gqa(attn_dtype dt, const void* Q, const void* K, const void
                          int64_t window_right, void* stream) {
   return attn::fwd_impl(dt, Q, K, V, O, lse, nullptr, attn::fixed_geometry(B, H, H_kv, N, d),
                         scale, mode, window_left, window_right, stream);
+}
+
+attn_status attn_fwd_persistent(attn_dtype dt, const void* Q, const void* K, const void* V,
+                                void* O, float* lse, int64_t B, int64_t H, int64_t H_kv,
+                                int64_t N, int64_t d, float scale, attn_mask_mode mode,
+                                int64_t window_left, int64_t window_right, void* stream) {
+  return attn::fwd_impl(dt, Q, K, V, O, lse, nullptr, attn::fixed_geometry(B, H, H_kv, N, d),
+                        scale, mode, window_left, window_right, stream, true);
 }
 
 attn_status attn_fwd_varlen(attn_dtype dt, const void* Q, const void* K, const void* V, void* O,

@@ -111,6 +111,23 @@ attn_status attn_fwd(attn_dtype dt, const void* Q, const void* K, const void* V,
 #define ATTN_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 
 /*
+ * attn_fwd_persistent -- attn_fwd_gqa with persistent scheduling (the pages'
+ * AI cores looping over their share of Q blocks, P1 §3.2 and §3.3 "AI Core
+ * count"): the grid holds only the workgroups the GPU runs at once, and each
+ * claims its next query block from a work queue per accelerator die until
+ * none is left, in the same die-local, heaviest-first order as attn_fwd.
+ * Same arguments, layouts, results (bit for bit) and errors as attn_fwd_gqa
+ * (H_kv = H: standard attention).  The queues are counters inside the
+ * library's code object, one set per GPU, which every launch leaves at zero:
+ * nothing to allocate or clear, but two attn_fwd_persistent launches must
+ * not run at the same time on one GPU (e.g. on two streams).
+ */
+attn_status attn_fwd_persistent(attn_dtype dt, const void* Q, const void* K, const void* V,
+                                void* O, float* lse, int64_t B, int64_t H, int64_t H_kv,
+                                int64_t N, int64_t d, float scale, attn_mask_mode mode,
+                                int64_t window_left, int64_t window_right, void* stream);
+
+/*
  * attn_bwd_workspace_bytes -- size in bytes of the device workspace attn_bwd
  * needs for these sizes: two float32 values per row (-D_i with
  * D_i = dO_i . O_i, and the row's lse rescaled to the score units the
