@@ -211,6 +211,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device copy of this many MiB (HBM counter calibration)")
+    ap.add_argument("--persistent", action="store_true",
+                    help="time attn_fwd_persistent (fixed-length workloads) instead of attn_fwd")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -239,7 +241,8 @@ def main():
         if w.packed:
             ea.attn_fwd_varlen(q, k, v, cu, max_len, mask=mask, scale=w.scale, out=o, lse=lse)
         else:
-            ea.attn_fwd(q, k, v, mask=mask, scale=w.scale, out=o, lse=lse)
+            ea.attn_fwd(q, k, v, mask=mask, scale=w.scale, out=o, lse=lse,
+                        persistent=args.persistent)
 
     for _ in range(args.warmup):
         step()
@@ -360,6 +363,10 @@ def main():
     }
     if backward is not None:
         rec["backward"] = backward
+    if args.persistent:
+        rec["entry_point"] = "attn_fwd_persistent"
+    if os.environ.get("EXACT_ATTN_LIB"):
+        rec["library"] = os.environ["EXACT_ATTN_LIB"]
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(w, inp)
     print(json.dumps(rec), flush=True)

@@ -14,7 +14,10 @@ import os
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+# The in-tree library; EXACT_ATTN_LIB may name another build of it (a tile-shape
+# variant from ``build --out``) for sweeps.
+_LIB_PATH = os.environ.get("EXACT_ATTN_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 _lib = None
 
 ATTN_F16, ATTN_BF16 = 0, 1

@@ -1,9 +1,14 @@
 """Build libattn.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
-    python -m exact_attention_14_amd.build
+    python -m exact_attention_14_amd.build [--define NAME=VALUE ...] [--out PATH]
 
 Sources are compiled in parallel into ``_build/`` at the repository root and
 linked into ``exact_attention_14_amd/libattn.so``.  Every call recompiles.
+``--define`` passes build parameters to every compile (the forward's tile
+shape: ATTN_FWD_BLOCK_K, ATTN_FWD_WAVES_NONE, ATTN_FWD_WAVES_MASKED; see
+csrc/plan.hpp) and ``--out`` writes such a variant elsewhere, e.g.
+``exact_attention_14_amd/variants/libattn_bc128.so``, which the binding loads
+when the environment variable EXACT_ATTN_LIB names it (tile-shape sweeps).
 """
 from __future__ import annotations
 
@@ -50,30 +55,48 @@ def _run(cmd):
     return r.stdout
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, defines=(), out: str = LIB) -> str:
+    tag = "".join(f"_{d}" for d in defines).replace("=", "")
+    build_dir = os.path.join(BUILD, "variant" + tag) if defines else BUILD
+    os.makedirs(build_dir, exist_ok=True)
+    dflags = [f"-D{d}" for d in defines]
     hipcc = _hipcc()
     jobs = []
     objs = []
     for src in HIP_SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
+        obj = os.path.join(build_dir, src + ".o")
         objs.append(obj)
-        jobs.append([hipcc, *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src),
-                     "-o", obj])
+        jobs.append([hipcc, *HIP_FLAGS, *dflags, *EXTRA_FLAGS.get(src, []), "-c",
+                     os.path.join(CSRC, src), "-o", obj])
     for src in CXX_SOURCES:
-        obj = os.path.join(BUILD, src + ".o")
+        obj = os.path.join(build_dir, src + ".o")
         objs.append(obj)
-        jobs.append(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append(["g++", *CXX_FLAGS, *dflags, "-c", os.path.join(CSRC, src), "-o", obj])
     workers = min(len(jobs), max(1, min(8, os.cpu_count() or 1)))
     with concurrent.futures.ThreadPoolExecutor(workers) as ex:
-        for out in ex.map(_run, jobs):
-            if verbose and out.strip():
-                print(out)
-    tmp = LIB + ".tmp"
+        for text in ex.map(_run, jobs):
+            if verbose and text.strip():
+                print(text)
+    os.makedirs(os.path.dirname(os.path.abspath(out)), exist_ok=True)
+    tmp = out + ".tmp"
     _run([hipcc, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def _main(argv) -> None:
+    import argparse
+    ap = argparse.ArgumentParser(description="build libattn.so for gfx950")
+    ap.add_argument("-v", action="store_true", help="print compiler output")
+    ap.add_argument("--define", action="append", default=[], metavar="NAME=VALUE",
+                    help="build parameter passed to every compile")
+    ap.add_argument("--out", default=LIB, help="library path to write")
+    a = ap.parse_args(argv)
+    for d in a.define:
+        if not d.startswith("ATTN_") or "=" not in d:
+            raise SystemExit(f"--define takes ATTN_NAME=VALUE, got {d!r}")
+    print(build(verbose=a.v, defines=a.define, out=a.out))
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    _main(sys.argv[1:])

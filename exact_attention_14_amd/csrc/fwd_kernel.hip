@@ -127,10 +127,14 @@ struct FwdLayout {
   // K and V go straight to LDS: each wavefront instruction fills 1 KiB.  K
   // rows have NCH + 1 slots of 16 bytes (the last one is padding).
   static constexpr int K_SLOTS = BC * (NCH + 1);
-  static constexpr int K_INSTR = K_SLOTS / 64;                 // 17 at d = 128, 9 at d = 64
+  // Whole 1 KiB loads: a K stage is rounded up to them (slots past the tile
+  // are filled from past the buffer, i.e. with zeros, and never read).
+  static constexpr int K_INSTR = (K_SLOTS + 63) / 64;          // 17 at d = 128, Bc = 64
+  static constexpr int K_ALLOC = K_INSTR * 1024;
   static constexpr int NW = NWAVES;
   static constexpr int K_INSTR_PER_WAVE = (K_INSTR + NW - 1) / NW;
-  static constexpr int V_WAVE_LOADS = V_BYTES / NW / 1024;
+  static constexpr int V_INSTR = V_BYTES / 1024;
+  static constexpr int V_WAVE_LOADS = (V_INSTR + NW - 1) / NW;
   static constexpr int V_ROWS_PER_1K = 1024 / (D * 2);
   static constexpr int VSWZ_MASK = NCH / 4 - 1;             // row bits used by the V swizzle
   static __device__ __forceinline__ int vswz(int row) { return (row & VSWZ_MASK) << 2; }
@@ -159,10 +163,11 @@ void fwd_kernel(FwdParams p, uint32_t n_wg) {
   constexpr int BR = fwd_block_q(MASK), BC = kFwdBlockK;
   constexpr int KSTEPS = D / 16;           // reduction steps over d
   constexpr int DBLK = D / 32;             // 32-row blocks of O^T
+  constexpr int KB = BC / 32;              // 32-key blocks of a tile
   constexpr uint32_t ROW_BYTES = D * 2;
   constexpr bool kOneSum = std::is_same<T, _Float16>::value;
 
-  __shared__ __attribute__((aligned(16))) char k_lds0[L::K_BYTES], k_lds1[L::K_BYTES];
+  __shared__ __attribute__((aligned(16))) char k_lds0[L::K_ALLOC], k_lds1[L::K_ALLOC];
   __shared__ __attribute__((aligned(16))) char v_lds0[L::V_BYTES], v_lds1[L::V_BYTES];
   __shared__ int slot_lds;
 
@@ -224,7 +229,7 @@ void fwd_kernel(FwdParams p, uint32_t n_wg) {
   float m = -INFINITY, l = 0.0f, lr = 0.0f;
   const float c = p.c;
 
-  static_assert(L::K_SLOTS % 64 == 0, "K tile must fill whole 1 KiB loads");
+  static_assert(L::V_BYTES % 1024 == 0, "V tile must fill whole 1 KiB loads");
   // K direct loads: instruction j (= wave + NW*i, NW wavefronts) fills 16-byte slots
   // s = 64j + lane of the stage; slot s holds row s / (NCH+1), chunk
   // s % (NCH+1).  Padding slots point past the end of the head, so the
@@ -234,7 +239,8 @@ void fwd_kernel(FwdParams p, uint32_t n_wg) {
   for (int i = 0; i < L::K_INSTR_PER_WAVE; ++i) {
     const int slot = (wave + L::NW * i) * 64 + lane;
     const int row = slot / (L::NCH + 1), ch = slot % (L::NCH + 1);
-    kg_off[i] = ch == L::NCH ? head_bytes : static_cast<uint32_t>(row) * ROW_BYTES + ch * 16;
+    const bool pad = ch == L::NCH || (L::K_SLOTS % 64 != 0 && row >= BC);
+    kg_off[i] = pad ? head_bytes : static_cast<uint32_t>(row) * ROW_BYTES + ch * 16;
   }
   // V direct loads: instruction j of wavefront w fills LDS bytes
   // [(NW*j + w) KiB, +1 KiB) of the stage, i.e. 16-byte slot s = 64*(NW*j+w) + lane
@@ -269,29 +275,30 @@ void fwd_kernel(FwdParams p, uint32_t n_wg) {
   auto gload_v_lds = [&](int t, char* dstb) {
 #pragma unroll
     for (int j = 0; j < L::V_WAVE_LOADS; ++j)
-      buf_load16_lds(rV, dstb + (L::NW * j + wave) * 1024, vg_off,
-                     static_cast<uint32_t>(t * BC + L::NW * j * L::V_ROWS_PER_1K) * ROW_BYTES);
+      if (L::V_INSTR % L::NW == 0 || L::NW * j + wave < L::V_INSTR)
+        buf_load16_lds(rV, dstb + (L::NW * j + wave) * 1024, vg_off,
+                       static_cast<uint32_t>(t * BC + L::NW * j * L::V_ROWS_PER_1K) * ROW_BYTES);
   };
 
   // S^T = K Q^T of tile t from a K stage: two independent accumulation chains.
-  auto scores = [&](const char* kb_, f32x16_t s[2]) {
-    s[0] = f32x16_t{};
-    s[1] = f32x16_t{};
+  auto scores = [&](const char* kb_, f32x16_t s[KB]) {
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) s[kb] = f32x16_t{};
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
         s[kb] = Elem<T>::mma(ld_lds16(kb_ + kr_off + kb * 32 * L::K_PITCH + kk * 32),
                              qf[kk], s[kb]);
   };
 
   // Phase 1 of tile t: mask (boundary tiles only), row max, and the online
   // rescale (rare).  Returns the exponent base.
-  auto apply_mask = [&](int t, f32x16_t s[2]) {
+  auto apply_mask = [&](int t, f32x16_t s[KB]) {
     const int k0 = t * BC;
     if (!tile_all_allowed(N, wq0, 32, k0, BC, MASK, p.wl, p.wr)) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = k0 + kb * 32 + (i >> 2) * 8 + half * 4 + (i & 3);
@@ -305,10 +312,10 @@ void fwd_kernel(FwdParams p, uint32_t n_wg) {
   };
   // Exact row max of the tile (rare path): raises the running max to it and
   // rescales the accumulator, l and l~.
-  auto raise_max = [&](f32x16_t s[2]) {
+  auto raise_max = [&](f32x16_t s[KB]) {
     float mx = -INFINITY;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
     mx = halves_max(mx);
@@ -327,21 +334,21 @@ void fwd_kernel(FwdParams p, uint32_t n_wg) {
   // the fp32 values (bf16 rounding, up to 2^-8 relative, is too coarse for
   // lse); for fp16 it is over the rounded values (at most 2^-11 relative,
   // well inside lse's tolerance), so that one sum serves as both l and l~.
-  // prob_pair handles pair pi (0..15: block pi / 8, elements 2j, 2j + 1).
-  auto prob_pair = [&](f32x16_t s[2], float base, uint32_t pk[2][8], float rsum[2], int pi) {
+  // prob_pair handles pair pi (0 .. 8 KB - 1: block pi / 8, elements 2j, 2j + 1).
+  auto prob_pair = [&](f32x16_t s[KB], float base, uint32_t pk[KB][8], float rsum[2], int pi) {
     const int kb = pi / 8, j = pi % 8;
     const float e0 = fast_exp2(fmaf(s[kb][2 * j], c, -base));
     const float e1 = fast_exp2(fmaf(s[kb][2 * j + 1], c, -base));
     pk[kb][j] = Elem<T>::pack2(e0, e1);
     if (kOneSum)
-      rsum[kb] = Elem<T>::add_pair(pk[kb][j], rsum[kb]);
+      rsum[kb % 2] = Elem<T>::add_pair(pk[kb][j], rsum[kb % 2]);
     else
-      rsum[kb] += e0 + e1;
+      rsum[kb % 2] += e0 + e1;
   };
-  auto softmax_exp = [&](f32x16_t s[2], float base, uint32_t pk[2][8]) -> float {
+  auto softmax_exp = [&](f32x16_t s[KB], float base, uint32_t pk[KB][8]) -> float {
     float rsum[2] = {0.0f, 0.0f};
 #pragma unroll
-    for (int pi = 0; pi < 16; ++pi) prob_pair(s, base, pk, rsum, pi);
+    for (int pi = 0; pi < 8 * KB; ++pi) prob_pair(s, base, pk, rsum, pi);
     return rsum[0] + rsum[1];
   };
 
@@ -352,32 +359,32 @@ void fwd_kernel(FwdParams p, uint32_t n_wg) {
   // three-deep ring; the scheduling barrier after each step keeps the
   // compiler from regrouping (left to itself it read each operand one
   // instruction ahead and waited on most reads).
-  auto scores_softmax = [&](const char* kb_, f32x16_t nxt[2], f32x16_t cur[2], float base,
-                            uint32_t pk[2][8]) -> float {
-    constexpr int PAIRS_PER_MMA = (16 + 2 * KSTEPS - 1) / (2 * KSTEPS);
+  auto scores_softmax = [&](const char* kb_, f32x16_t nxt[KB], f32x16_t cur[KB], float base,
+                            uint32_t pk[KB][8]) -> float {
+    constexpr int PAIRS_PER_MMA = (8 + KSTEPS - 1) / KSTEPS;
     float rsum[2] = {0.0f, 0.0f};
-    nxt[0] = f32x16_t{};
-    nxt[1] = f32x16_t{};
-    u32x4_t kop[3][2];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) nxt[kb] = f32x16_t{};
+    u32x4_t kop[3][KB];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
         kop[kk][kb] = ld_lds16(kb_ + kr_off + kb * 32 * L::K_PITCH + kk * 32);
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
       if (kk + 2 < KSTEPS) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
           kop[(kk + 2) % 3][kb] = ld_lds16(kb_ + kr_off + kb * 32 * L::K_PITCH + (kk + 2) * 32);
       }
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
         nxt[kb] = Elem<T>::mma(kop[kk % 3][kb], qf[kk], nxt[kb]);
 #pragma unroll
         for (int r = 0; r < PAIRS_PER_MMA; ++r) {
-          const int pi = 2 * kk + kb + r * 2 * KSTEPS;
-          if (pi < 16) prob_pair(cur, base, pk, rsum, pi);
+          const int pi = KB * kk + kb + r * KB * KSTEPS;
+          if (pi < 8 * KB) prob_pair(cur, base, pk, rsum, pi);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -388,7 +395,7 @@ void fwd_kernel(FwdParams p, uint32_t n_wg) {
   // Phase 3: O^T += V^T P^T over four 16-key steps, the DBLK chains
   // interleaved, with V^T operands read one step ahead (double-buffered), and
   // the row sum of the rounded probabilities.
-  auto pv_sums = [&](const char* vb_, uint32_t pk[2][8]) {
+  auto pv_sums = [&](const char* vb_, uint32_t pk[KB][8]) {
     auto vread = [&](int ks, int db) {
       const char* va = vb_ + vr_off[db] + ks * 16 * L::V_PITCH;
       const u32x2_t lo2 = ld_lds_tr8(va);
@@ -426,7 +433,7 @@ void fwd_kernel(FwdParams p, uint32_t n_wg) {
   // and V of tile t+1 travel from HBM straight into the LDS stages freed one
   // iteration ago.  The scores of the (nonexistent) tile after the last are
   // computed from whatever the stage holds and never used.
-  f32x16_t sA[2], sB[2];
+  f32x16_t sA[KB], sB[KB];
   gload_k_lds(lo, k_lds0);
   gload_v_lds(lo, v_lds0);
   if (lo + 1 < hi) gload_k_lds(lo + 1, k_lds1);
@@ -438,13 +445,13 @@ void fwd_kernel(FwdParams p, uint32_t n_wg) {
   __syncthreads();
 
   // One pipeline step; P = (t - lo) % 2 selects the stages at compile time.
-  auto step = [&](auto P_, int t, f32x16_t cur[2], f32x16_t nxt[2]) {
+  auto step = [&](auto P_, int t, f32x16_t cur[KB], f32x16_t nxt[KB]) {
     constexpr int P = decltype(P_)::value;
     const bool has1 = t + 1 < hi, has2 = t + 2 < hi;
     if (has2) gload_k_lds(t + 2, P ? k_lds1 : k_lds0);
     if (has1) gload_v_lds(t + 1, P ? v_lds0 : v_lds1);
     apply_mask(t, cur);
-    uint32_t pk[2][8];
+    uint32_t pk[KB][8];
     float rs = scores_softmax(P ? k_lds0 : k_lds1, nxt, cur, m == -INFINITY ? 0.0f : m, pk);
     // Optimistic softmax: the probabilities used the running max; if one of
     // them exceeds 2^kTau (their sum does) or the row has no max yet, take
@@ -495,7 +502,7 @@ template <typename T, int D, int MASK>
 hipError_t launch_one(const FwdParams& p, int64_t n_wg, int persist_cus, hipStream_t stream) {
   // Pairs help fixed-length batches (+3.4% at B4 H32 H_kv8 N4096 causal); a
   // packed batch's many short items run better in four-wavefront workgroups.
-  if (MASK != kNone && p.g.group % 2 == 0 && p.g.cu_seqlens == nullptr) {
+  if (MASK != kNone && fwd_waves(MASK) == 4 && p.g.group % 2 == 0 && p.g.cu_seqlens == nullptr) {
     if (persist_cus > 0)
       hipLaunchKernelGGL((fwd_kernel<T, D, MASK, true, true>),
                          dim3(persistent_grid(n_wg / 2, 8, persist_cus)), dim3(64 * 8), 0, stream, p,

@@ -25,9 +25,28 @@ enum MaskMode : int { kNone = 0, kCausal = 1, kSliding = 2 };
 // Without a mask a workgroup has 8 wavefronts (256 query rows) so that each
 // K/V tile is fetched once for more rows; with a causal or sliding mask it
 // has 4 (128 rows), whose finer work items balance the unequal row lengths
-// and waste fewer products on tiles past a wavefront's band.
-constexpr int kFwdBlockK = 64;
-ATTN_HD constexpr int fwd_waves(int mode) { return mode == 0 ? 8 : 4; }
+// and waste fewer products on tiles past a wavefront's band.  The three are
+// build parameters (ATTN_FWD_BLOCK_K: 32, 64 or 128; ATTN_FWD_WAVES_NONE,
+// ATTN_FWD_WAVES_MASKED: 4 or 8) so that the tile-shape sweep can build other
+// shapes; the defaults are the ones the sweep chose.
+#ifndef ATTN_FWD_BLOCK_K
+#define ATTN_FWD_BLOCK_K 64
+#endif
+#ifndef ATTN_FWD_WAVES_NONE
+#define ATTN_FWD_WAVES_NONE 8
+#endif
+#ifndef ATTN_FWD_WAVES_MASKED
+#define ATTN_FWD_WAVES_MASKED 4
+#endif
+static_assert(ATTN_FWD_BLOCK_K == 32 || ATTN_FWD_BLOCK_K == 64 || ATTN_FWD_BLOCK_K == 128,
+              "key tile of 32, 64 or 128 rows");
+static_assert((ATTN_FWD_WAVES_NONE == 4 || ATTN_FWD_WAVES_NONE == 8) &&
+                  (ATTN_FWD_WAVES_MASKED == 4 || ATTN_FWD_WAVES_MASKED == 8),
+              "4 or 8 wavefronts per workgroup");
+constexpr int kFwdBlockK = ATTN_FWD_BLOCK_K;
+ATTN_HD constexpr int fwd_waves(int mode) {
+  return mode == 0 ? ATTN_FWD_WAVES_NONE : ATTN_FWD_WAVES_MASKED;
+}
 ATTN_HD constexpr int fwd_block_q(int mode) { return 32 * fwd_waves(mode); }
 
 // Backward: the dQ pass mirrors the forward (query-major); the dK/dV pass is

@@ -3,6 +3,7 @@
     python -m exact_attention_14_amd.profiles stats  <kernel_stats.csv> <out.md> <command...>
     python -m exact_attention_14_amd.profiles traffic <fetch_dir> <write_dir> <workload> <copy_mib> <out.json> <out.md>
     python -m exact_attention_14_amd.profiles counters [--clock-ghz=F] <counter_dir> <kernel_stats.csv> <out.md> <command...>
+    python -m exact_attention_14_amd.profiles sweep <out.md> <title> <commands> <label:flop:dir>...
 
 ``stats`` turns the ``*_kernel_stats.csv`` of ``rocprofv3 --kernel-trace --stats
 --output-format csv`` into a short markdown table.  ``traffic`` reads two
@@ -151,6 +152,72 @@ def counters(counter_dir: str, kernel_stats: str, out_md: str, command: str,
         f.write("\n".join(lines))
 
 
+def _pmc_means(dirname: str, key: str = "fwd_kernel"):
+    """Counter -> mean per dispatch of kernel `key` over every pass CSV under dirname."""
+    per = {}
+    for path in glob.glob(os.path.join(dirname, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            if key not in r["Kernel_Name"]:
+                continue
+            d = per.setdefault(r["Counter_Name"], {})
+            d[(path, r["Dispatch_Id"])] = d.get((path, r["Dispatch_Id"]), 0.0) + float(
+                r["Counter_Value"])
+    return {k: sum(v.values()) / len(v) for k, v in per.items()}
+
+
+def _trace_us(dirname: str, key: str = "fwd_kernel") -> float:
+    for path in glob.glob(os.path.join(dirname, "**", "*kernel_stats.csv"), recursive=True):
+        for r in csv.DictReader(open(path)):
+            if key in r["Name"]:
+                return float(r["AverageNs"]) / 1e3
+    raise SystemExit(f"no {key} in the kernel statistics under {dirname}")
+
+
+def sweep(out_md: str, title: str, commands: str, entries) -> None:
+    """One table row per tile-shape variant: `label:flop_per_launch:dir`, where dir
+    holds the kernel trace and the counter passes of that variant's bench run."""
+    rows = []
+    for e in entries:
+        label, flop, d = e.split(":", 2)
+        us = _trace_us(d)
+        m = _pmc_means(d)
+        mfma = m.get("SQ_INSTS_MFMA", float("nan"))
+        busy = m.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) / 1024  # per SIMD
+        wave_cyc = m.get("SQ_WAVE_CYCLES", float("nan"))
+        hit, miss = m.get("TCC_HIT_sum", float("nan")), m.get("TCC_MISS_sum", float("nan"))
+        rows.append([
+            label, f"{us:.1f}", f"{float(flop) / (us * 1e-6) / 1e12:.0f}",
+            f"{busy / us:.0f}",
+            f"{m.get('SQ_INSTS_VALU', float('nan')) / mfma:.2f}",
+            f"{m.get('SQ_INSTS_VALU_TRANS_F32', float('nan')) / mfma:.2f}",
+            f"{m.get('SQ_INSTS_LDS', float('nan')) / mfma:.2f}",
+            f"{m.get('SQ_LDS_BANK_CONFLICT', float('nan')):.3g}",
+            f"{m.get('SQ_WAIT_INST_ANY', float('nan')) / wave_cyc:.0%}",
+            f"{m.get('SQ_WAIT_ANY', float('nan')) / wave_cyc:.0%}",
+            f"{m.get('SQ_ACTIVE_INST_ANY', float('nan')) / wave_cyc:.0%}",
+            f"{m.get('SQ_VALU_MFMA_COEXEC_CYCLES', float('nan')) / max(busy * 1024, 1):.0%}",
+            f"{hit / (hit + miss):.1%}",
+        ])
+    hdr = ["variant", "fwd_kernel us", "TFLOP/s", "MFMA busy cycles per SIMD per us",
+           "VALU / MFMA instr", "exp2 / MFMA", "LDS / MFMA instr", "LDS bank conflict cycles",
+           "ready, not issued (of wave cycles)", "waiting", "issuing", "VALU co-issued "
+           "beside busy MFMA (of MFMA busy)", "L2 hit rate"]
+    lines = [f"# {title}", "", "Commands (per variant; the library from `python -m "
+             "exact_attention_14_amd.build --define ... --out ...`):", "", commands, "",
+             "Kernel time: average of the rocprofv3 kernel trace; counters: means per dispatch of "
+             "separate `--pmc` passes of the same command.  MFMA busy cycles per SIMD per us is the "
+             "busy fraction times the shader clock in MHz (no clock counter is read; at the "
+             "~2.0 GHz this load settles at, 1000 = 50%).  The wave-cycle fractions divide "
+             "SQ_WAIT_INST_ANY (ready but not issued), SQ_WAIT_ANY (waiting on a dependency, "
+             "s_waitcnt or a barrier) and SQ_ACTIVE_INST_ANY (issuing) by SQ_WAVE_CYCLES, all in "
+             "the same units.",
+             "", "| " + " | ".join(hdr) + " |", "|" + "---|" * len(hdr)]
+    lines += ["| " + " | ".join(r) + " |" for r in rows]
+    lines.append("")
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines))
+
+
 if __name__ == "__main__":
     if sys.argv[1] == "stats":
         stats(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
@@ -161,6 +228,8 @@ if __name__ == "__main__":
             clk = float(args[0].split("=", 1)[1])
             args = args[1:]
         counters(args[0], args[1], args[2], " ".join(args[3:]), clk)
+    elif sys.argv[1] == "sweep":
+        sweep(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5:])
     elif sys.argv[1] == "traffic":
         traffic(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5]), sys.argv[6], sys.argv[7])
     else:
