@@ -39,12 +39,16 @@
 //   against the running max m as it stands, without taking the tile's own
 //   row max.  If none of them exceeds 2^kTau (checked through the lane's sum
 //   of them, an upper bound) they are kept: m need not be the exact max, since
-//   it cancels between the numerator and l, and probabilities up to 2^kTau fit
-//   both fp16 and bf16.  Otherwise (and while a row has no m yet) the exact
-//   tile max is taken, m is raised to it, the accumulator, l and l~ are
-//   rescaled (P1 §2.3: the rescale corrects history when the max moves) and
-//   the tile's probabilities are formed again.  Nearly every tile takes the
-//   first path and skips both the row max and the rescale.
+//   it cancels between the numerator and l.  kTau is as large as the 16-bit
+//   type allows: 15 for fp16 (2^15 < 65504), 64 for bf16, whose rounding is
+//   2^-9 relative at any magnitude up to 2^127 (with 2^64 per probability the
+//   fp32 sums stay far below their range).  Otherwise (and while a row has no
+//   m yet) the exact tile max is taken, m is raised to it, the accumulator, l
+//   and l~ are rescaled (P1 §2.3: the rescale corrects history when the max
+//   moves) and the tile's probabilities are formed again.  Nearly every tile
+//   takes the first path and skips both the row max and the rescale; a large
+//   kTau keeps it so when a few outlier keys raise the row max far above the
+//   rest.
 // * Whole key tiles outside the mask's band are never visited (P1 §3.3 (4));
 //   only tiles that straddle the band edge or the ragged end of the sequence
 //   evaluate the mask per element, with -inf (P2 "pitfall 1": ragged lengths;
@@ -67,7 +71,10 @@
 namespace attn {
 namespace {
 
-constexpr float kSumBound = 256.0f;  // 2^kTau, kTau = 8
+// 2^kTau, the bound on a probability formed against the running max (see the
+// file comment): kTau = 15 for fp16, 64 for bf16.
+template <typename T>
+constexpr float kSumBound = std::is_same<T, _Float16>::value ? 32768.0f : 18446744073709551616.0f;
 
 // Work queues of the persistent forward (fwd_kernel with PERSIST): the next unclaimed
 // slot of each die's run of work items, and the number of workgroups that
@@ -456,7 +463,7 @@ void fwd_kernel(FwdParams p, uint32_t n_wg) {
     // Optimistic softmax: the probabilities used the running max; if one of
     // them exceeds 2^kTau (their sum does) or the row has no max yet, take
     // the exact tile max, rescale and recompute (rare).
-    if (__any(!(rs <= kSumBound) || m == -INFINITY)) {
+    if (__any(!(rs <= kSumBound<T>) || m == -INFINITY)) {
       raise_max(cur);
       rs = softmax_exp(cur, m == -INFINITY ? 0.0f : m, pk);
     }

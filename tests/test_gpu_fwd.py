@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import exact_attention_14_amd as ea
-from parity_util import check_fwd, fwd_case, gpu, say
+from parity_util import check_fwd, fwd_case, gpu, oracle_mask, run_fwd, say
 from workloads import SINGLE_HEAD_N256, draw, make_inputs, to_f64
 
 import oracle
@@ -61,6 +61,41 @@ def test_outlier_keys_move_the_running_max():
     say("outlier keys, N=2048 causal and none")
     for mask in [None, "causal"]:
         fwd_case(1, 4, 2048, 128, "bf16", mask, seed=99, outlier_frac=0.01, outlier_mul=8.0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("mask", [None, "causal"])
+def test_running_max_jumps_beyond_the_optimistic_bound(dtype, mask):
+    """Scores that rise in steps far larger than the optimistic bound on a
+    probability (2^64 for bf16, 2^15 for fp16, in exp2 units): every step must
+    take the exact-max path (a probability formed against the old max would
+    overflow), and smaller steps below the bound must not disturb the result.
+    Q rows are all e_0 and K's first column rises in steps within and across
+    key tiles, so each row's softmax concentrates on its latest keys."""
+    N, d = 700, 64
+    inp = draw(1, 2, N, d, dtype, 77)
+    q, k, v = inp["q"].clone(), inp["k"].clone(), inp["v"].clone()
+    q.zero_()
+    q[..., 0] = 1.0
+    k[..., 0] = 0.0
+    # scale 1: score = k[:, 0]; exp2 units multiply by log2(e) = 1.44
+    steps = {100: 30.0, 160: 60.0, 161: 64.0, 300: 120.0, 333: 124.0, 500: 200.0, 640: 204.0}
+    level = 0.0
+    for j in range(N):
+        level = steps.get(j, level)
+        k[..., j, 0] = level
+    if dtype == "f16":  # keep the largest score (and q.k) inside fp16's range
+        k[..., 0] = k[..., 0] / 8.0
+    scale = 1.0
+    o, lse = run_fwd({"q": q, "k": k, "v": v}, mask, scale)
+    name, wl, wr = oracle_mask(mask)
+    O_ref = np.empty((2, N, d))
+    L_ref = np.empty((2, N))
+    for h in range(2):
+        O_ref[h], L_ref[h] = oracle.forward_head(to_f64(q[0, h]), to_f64(k[0, h]), to_f64(v[0, h]),
+                                                 scale, name, wl, wr)
+    check_fwd(to_f64(o[0].cpu()), lse[0].cpu().double().numpy(), O_ref, L_ref,
+              label=f"max jumps {dtype} {mask}")
 
 
 @pytest.mark.parametrize("scale", [-0.3, 0.0, 1.7, 1e-3])
