@@ -332,7 +332,7 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
   const uint32_t slice = blockIdx.x % p.kv_split, item = blockIdx.x / p.kv_split;
   int64_t head, kblk;
   if (p.g.cu_seqlens == nullptr) {
-    kv_item(item, p.n_kv_heads, n_kblk, MASK, &head, &kblk);
+    kv_item(item, p.n_kv_heads, n_kblk, MASK, p.g.group == 1, &head, &kblk);
   } else {
     const int H_kv = p.g.H / p.g.group;
     packed_item(item, H_kv, p.n_kv_heads / H_kv, n_kblk, MASK == kCausal, &head, &kblk);

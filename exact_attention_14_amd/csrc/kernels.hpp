@@ -90,9 +90,9 @@ __device__ __forceinline__ void fwd_item(uint32_t wg, uint32_t n_heads, uint32_t
 }
 
 __device__ __forceinline__ void kv_item(uint32_t wg, uint32_t n_heads, uint32_t n_blk, int mode,
-                                        int64_t* head, int64_t* blk) {
+                                        bool grouped, int64_t* head, int64_t* blk) {
   uint32_t h, b;
-  kv_work_item<uint32_t>(wg, n_heads, n_blk, mode, &h, &b);
+  kv_work_item<uint32_t>(wg, n_heads, n_blk, mode, &h, &b, grouped);
   *head = h;
   *blk = b;
 }

@@ -258,16 +258,35 @@ ATTN_HD void packed_work_item(I wg, I heads, I n_seqs, I n_blk, bool ascending, 
 
 // Work item -> (head, key block) of the backward's key-major pass.  Under a
 // causal mask key block b sees every query tile from b on, so block 0 does
-// up to 16 times the work of the last one at N = 4096: the order is then
-// block-major, every head's heaviest block first.  Consecutive ids go to the
-// dies in turn, so id % n_heads = head keeps each head on one die when the
-// head count is a multiple of kNumXcd.  Other masks give every key block
-// about the same work and keep the head-major order of fwd_work_item, where
-// the blocks of a head run side by side and share its streamed Q/dO tiles in
-// L2.
+// up to 16 times the work of the last one at N = 4096: the order runs the
+// heaviest blocks first.  Consecutive ids go to the dies in turn.  For
+// standard multi-head attention (`grouped`) with the head count a multiple
+// of kNumXcd * kBwdKvHeadGroup, die x takes the heads h with
+// h % kNumXcd == x, kBwdKvHeadGroup of them at a time, block-major (heaviest
+// block first) within each group, so that the workgroups running on a die
+// at once read the Q/dO tiles of a few heads (+1.9% at B8 H40 N4096, groups
+// of 4; groups of 1 and 2 measured -1.7% and 0%, and with key/value heads
+// shared by several query heads grouping lost 0.6-18%).  Otherwise the order
+// is block-major over all heads, with id % n_heads = head (which keeps a
+// head on one die when the head count is a multiple of kNumXcd).
+// Other masks give every key block about the same work and keep the
+// head-major order of fwd_work_item, where the blocks of a head run side by
+// side and share its streamed Q/dO tiles in L2.
+constexpr int kBwdKvHeadGroup = 4;
 template <typename I>
-ATTN_HD void kv_work_item(I wg, I n_heads, I n_kblk, int mode, I* head, I* kblk) {
+ATTN_HD void kv_work_item(I wg, I n_heads, I n_kblk, int mode, I* head, I* kblk,
+                          bool grouped = true) {
   if (mode == kCausal) {
+    const I G = static_cast<I>(kBwdKvHeadGroup);
+    if (grouped && n_heads % (kNumXcd * G) == 0) {
+      const I x = wg % kNumXcd, s = wg / kNumXcd;
+      const I per_group = G * n_kblk;
+      const I grp = s / per_group, r = s - grp * per_group;
+      const I kb = r / G;
+      *kblk = kb;
+      *head = x + kNumXcd * (grp * G + (r - kb * G));
+      return;
+    }
     *kblk = wg / n_heads;
     *head = wg - *kblk * n_heads;
   } else {

@@ -359,11 +359,15 @@ attn_status attn_fwd_workgroup(int64_t wg, int64_t n_heads, int64_t n_qblk, attn
 
 /*
  * attn_bwd_kv_workgroup -- which (head index b*H + h, key block) workgroup
- * `wg` of the backward's key-major dK/dV pass (n_wg = B*H*n_kblk) processes.
- * With a causal mask the order is key-block-major, all heads' first (most
- * loaded: it sees every query tile) key blocks first; otherwise it is the
- * forward's head-major order.  Returns ATTN_E_SHAPE if wg is out of range,
- * ATTN_E_MASK for an unknown mode, ATTN_E_NULLPTR for null outputs.
+ * `wg` of the backward's key-major dK/dV pass (n_wg = B*H*n_kblk) processes
+ * for standard multi-head attention.  Workgroups are dealt to the 8
+ * accelerator dies round-robin.  With a causal mask and a head count that is
+ * a multiple of 32, die x runs the heads h with h % 8 == x, four at a time,
+ * each group's heaviest key block (it sees every query tile) first; with a
+ * causal mask otherwise the order is key-block-major over all heads;
+ * without one it is the forward's head-major order.  Returns ATTN_E_SHAPE if
+ * wg is out of range, ATTN_E_MASK for an unknown mode, ATTN_E_NULLPTR for
+ * null outputs.
  */
 attn_status attn_bwd_kv_workgroup(int64_t wg, int64_t n_heads, int64_t n_kblk,
                                   attn_mask_mode mode, int64_t* head, int64_t* kblk);

@@ -258,16 +258,28 @@ def test_kv_workgroup_order_is_a_bijection(n_heads, n_kblk, mode):
 
 
 def test_causal_kv_order_is_heavy_first_and_keeps_heads_on_one_die():
-    """Causal: key block 0 (every query tile) of every head first, then block 1 ...;
-    ids are dealt round-robin to 8 dies, and with 320 heads each head stays on one."""
+    """Causal: ids are dealt round-robin to 8 dies; with 320 heads die x runs the
+    heads h = x (mod 8), four at a time, key block 0 (every query tile) of the
+    four first, then block 1, ...; with 7 heads (no grouping) block-major over all."""
     n_heads, n_kblk = 320, 16
-    die_heads, prev = {}, -1
+    die_heads = {}
+    per_die = {}
     for wg in range(n_heads * n_kblk):
         h, kb = ea.attn_bwd_kv_workgroup(wg, n_heads, n_kblk, 1)
-        assert kb >= prev
-        prev = kb
+        assert h % 8 == wg % 8
         die_heads.setdefault(h, set()).add(wg % 8)
+        per_die.setdefault(wg % 8, []).append((h, kb))
     assert all(len(d) == 1 for d in die_heads.values())
+    for seq in per_die.values():
+        for g in range(0, len(seq), 4 * n_kblk):
+            grp = seq[g:g + 4 * n_kblk]
+            assert len({h for h, _ in grp}) == 4          # one group of four heads ...
+            assert [kb for _, kb in grp] == sorted(kb for _, kb in grp)  # ... heaviest first
+    prev = -1
+    for wg in range(7 * 5):
+        h, kb = ea.attn_bwd_kv_workgroup(wg, 7, 5, 1)
+        assert kb >= prev and h == wg % 7
+        prev = kb
     # other masks: the forward's head-major order
     for wg in (0, 17, 5119):
         assert ea.attn_bwd_kv_workgroup(wg, n_heads, n_kblk, 0) == ea.attn_fwd_workgroup(
