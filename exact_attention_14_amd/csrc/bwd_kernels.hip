@@ -530,8 +530,8 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
   // dK = scale * dS^T Q with the signed scale; dV = P^T dO.  A split group
   // leaves its fp32 partial sums (unscaled) for the reduction instead.
   acc_fence(dv);
-  acc_fence(dk);
   if (p.kv_split > 1) {
+    acc_fence(dk);
     const size_t part = (static_cast<size_t>(slice) * p.kv_rows + kr.kv_row0) * D;
     const uint32_t part_bytes = static_cast<uint32_t>(N) * D * 4;
     const auto rpK = make_rsrc(p.dK_part + part, part_bytes);
@@ -557,6 +557,21 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
   const float sc = p.scale;
   const auto rdK = make_rsrc(reinterpret_cast<char*>(p.dK) + kvoff, head_bytes);
   const auto rdV = make_rsrc(reinterpret_cast<char*>(p.dV) + kvoff, head_bytes);
+  // dV first, then dK (fenced only now): fewer values are live at once.
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x16_t& b_ = dv[kb * DBLK + db];
+        const uint32_t off =
+            static_cast<uint32_t>(kcol[kb]) * ROWB + (db * 32 + g * 8 + half * 4) * 2;
+        const u32x2_t b = {Elem<T>::pack2(b_[g * 4 + 0], b_[g * 4 + 1]),
+                           Elem<T>::pack2(b_[g * 4 + 2], b_[g * 4 + 3])};
+        buf_store8(b, rdV, off);
+      }
+  acc_fence(dk);
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -564,15 +579,11 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x16_t& a_ = dk[kb * DBLK + db];
-        const f32x16_t& b_ = dv[kb * DBLK + db];
         const uint32_t off =
             static_cast<uint32_t>(kcol[kb]) * ROWB + (db * 32 + g * 8 + half * 4) * 2;
         const u32x2_t a = {Elem<T>::pack2(a_[g * 4 + 0] * sc, a_[g * 4 + 1] * sc),
                            Elem<T>::pack2(a_[g * 4 + 2] * sc, a_[g * 4 + 3] * sc)};
-        const u32x2_t b = {Elem<T>::pack2(b_[g * 4 + 0], b_[g * 4 + 1]),
-                           Elem<T>::pack2(b_[g * 4 + 2], b_[g * 4 + 3])};
         buf_store8(a, rdK, off);
-        buf_store8(b, rdV, off);
       }
 }
 
