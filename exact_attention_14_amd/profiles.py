@@ -1,9 +1,9 @@
 """Summaries of rocprofv3 output for the committed profiles/ folder.
 
     python -m exact_attention_14_amd.profiles stats  <kernel_stats.csv> <out.md> <command...>
-    python -m exact_attention_14_amd.profiles traffic <fetch_dir> <write_dir> <workload> <copy_mib> <out.json> <out.md>
+    python -m exact_attention_14_amd.profiles traffic <fetch_dir> <write_dir> <workload> <copy_mib> <out.json> <out.md> <commands...>
     python -m exact_attention_14_amd.profiles counters [--clock-ghz=F] <counter_dir> <kernel_stats.csv> <out.md> <command...>
-    python -m exact_attention_14_amd.profiles sweep <out.md> <title> <commands> <label:flop:dir>...
+    python -m exact_attention_14_amd.profiles sweep <out.md> <title> <commands> <label:flop:dir[:kernel]>...
 
 ``stats`` turns the ``*_kernel_stats.csv`` of ``rocprofv3 --kernel-trace --stats
 --output-format csv`` into a short markdown table.  ``traffic`` reads two
@@ -79,12 +79,14 @@ def _counter(dirname: str, counter: str):
 
 
 def traffic(fetch_dir: str, write_dir: str, workload: str, copy_mib: int, out_json: str,
-            out_md: str) -> None:
+            out_md: str, commands: str = "") -> None:
     copy_bytes = copy_mib * (1 << 20)
     out = {"workload": workload, "kernel_source_sha": kernel_source_sha(), "copy_mib": copy_mib}
     lines = ["# HBM traffic of the forward kernel (rocprofv3 PMC)", "",
              f"Workload: `{workload}`.  Counters in KiB per dispatch, scaled by the same counter",
              f"read for a device copy of {copy_mib} MiB (reads and writes exactly that).", ""]
+    if commands:
+        lines += [f"Commands: {commands}", ""]
     total = 0.0
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         fwd, copy = _counter(d, counter)
@@ -174,13 +176,15 @@ def _trace_us(dirname: str, key: str = "fwd_kernel") -> float:
 
 
 def sweep(out_md: str, title: str, commands: str, entries) -> None:
-    """One table row per tile-shape variant: `label:flop_per_launch:dir`, where dir
-    holds the kernel trace and the counter passes of that variant's bench run."""
+    """One table row per `label:flop_per_launch:dir[:kernel]`, where dir holds the
+    kernel trace and the counter passes of one bench run and kernel (default
+    fwd_kernel) names the kernel of the row."""
     rows = []
     for e in entries:
-        label, flop, d = e.split(":", 2)
-        us = _trace_us(d)
-        m = _pmc_means(d)
+        label, flop, d, *key = e.split(":")
+        key = key[0] if key else "fwd_kernel"
+        us = _trace_us(d, key)
+        m = _pmc_means(d, key)
         mfma = m.get("SQ_INSTS_MFMA", float("nan"))
         busy = m.get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) / 1024  # per SIMD
         wave_cyc = m.get("SQ_WAVE_CYCLES", float("nan"))
@@ -198,12 +202,11 @@ def sweep(out_md: str, title: str, commands: str, entries) -> None:
             f"{m.get('SQ_VALU_MFMA_COEXEC_CYCLES', float('nan')) / max(busy * 1024, 1):.0%}",
             f"{hit / (hit + miss):.1%}",
         ])
-    hdr = ["variant", "fwd_kernel us", "TFLOP/s", "MFMA busy cycles per SIMD per us",
+    hdr = ["variant", "kernel us", "TFLOP/s", "MFMA busy cycles per SIMD per us",
            "VALU / MFMA instr", "exp2 / MFMA", "LDS / MFMA instr", "LDS bank conflict cycles",
            "ready, not issued (of wave cycles)", "waiting", "issuing", "VALU co-issued "
            "beside busy MFMA (of MFMA busy)", "L2 hit rate"]
-    lines = [f"# {title}", "", "Commands (per variant; the library from `python -m "
-             "exact_attention_14_amd.build --define ... --out ...`):", "", commands, "",
+    lines = [f"# {title}", "", "Commands:", "", commands, "",
              "Kernel time: average of the rocprofv3 kernel trace; counters: means per dispatch of "
              "separate `--pmc` passes of the same command.  MFMA busy cycles per SIMD per us is the "
              "busy fraction times the shader clock in MHz (no clock counter is read; at the "
@@ -231,6 +234,7 @@ if __name__ == "__main__":
     elif sys.argv[1] == "sweep":
         sweep(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5:])
     elif sys.argv[1] == "traffic":
-        traffic(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5]), sys.argv[6], sys.argv[7])
+        traffic(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5]), sys.argv[6], sys.argv[7],
+                " ".join(sys.argv[8:]))
     else:
         raise SystemExit(__doc__)

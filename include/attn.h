@@ -352,7 +352,9 @@ attn_status attn_kv_tile_range(int64_t N, int64_t q0, int64_t block_q, int64_t b
  * workgroup `wg` of `n_wg` = B*H*n_qblk processes: workgroups are dealt to the
  * 8 accelerator dies round-robin, so consecutive ids are remapped to keep all
  * query blocks of one head on one die's L2; causal masks also run the longest
- * query blocks first.  Returns ATTN_E_SHAPE if wg is out of range.
+ * query blocks first, four heads at a time (the last block of each of the four,
+ * then the second-to-last of each, ...).  Returns ATTN_E_SHAPE if wg is out of
+ * range.
  */
 attn_status attn_fwd_workgroup(int64_t wg, int64_t n_heads, int64_t n_qblk, attn_mask_mode mode,
                                int64_t* head, int64_t* qblk);

@@ -293,6 +293,32 @@ def test_causal_runs_longest_query_blocks_first():
     assert qb0 == 0
 
 
+@pytest.mark.parametrize("n_heads", [128, 320, 6])
+def test_causal_order_runs_four_heads_at_a_time(n_heads):
+    """Causal: ids are dealt round-robin to 8 dies and die x runs a contiguous run of
+    the item sequence, so die 0's items, then die 1's, ... give that sequence.  It
+    takes four consecutive heads at a time (a short last chunk alike): the last
+    query block of each of the four, then the second-to-last of each, ..."""
+    n_qblk = 32
+    per_die = {}
+    for wg in range(n_heads * n_qblk):
+        per_die.setdefault(wg % 8, []).append(ea.attn_fwd_workgroup(wg, n_heads, n_qblk, 1))
+    seq = [hq for x in range(8) for hq in per_die.get(x, [])]
+    assert sorted(seq) == sorted((h, qb) for h in range(n_heads) for qb in range(n_qblk))
+    pos = 0
+    for c in range(0, n_heads, 4):
+        nh = min(4, n_heads - c)
+        grp = seq[pos:pos + nh * n_qblk]
+        pos += nh * n_qblk
+        assert [h for h, _ in grp] == [c + r % nh for r in range(nh * n_qblk)]
+        assert [qb for _, qb in grp] == [n_qblk - 1 - r // nh for r in range(nh * n_qblk)]
+    if n_heads % 8 == 0:  # whole heads per die
+        dies = {}
+        for wg in range(n_heads * n_qblk):
+            dies.setdefault(ea.attn_fwd_workgroup(wg, n_heads, n_qblk, 1)[0], set()).add(wg % 8)
+        assert all(len(d) == 1 for d in dies.values())
+
+
 def test_binding_rejects_host_tensors_before_any_library_call():
     """CPU tensors never reach the kernels: the binding raises first."""
     import torch
