@@ -3,7 +3,7 @@
     python -m exact_attention_14_amd.profiles stats  <kernel_stats.csv> <out.md> <command...>
     python -m exact_attention_14_amd.profiles traffic <fetch_dir> <write_dir> <workload> <copy_mib> <out.json> <out.md> <commands...>
     python -m exact_attention_14_amd.profiles counters [--clock-ghz=F] <counter_dir> <kernel_stats.csv> <out.md> <command...>
-    python -m exact_attention_14_amd.profiles sweep <out.md> <title> <commands> <label:flop:dir[:kernel]>...
+    python -m exact_attention_14_amd.profiles sweep [--rows=NAME] <out.md> <title> <commands> <label:flop:dir[:kernel]>...
 
 ``stats`` turns the ``*_kernel_stats.csv`` of ``rocprofv3 --kernel-trace --stats
 --output-format csv`` into a short markdown table.  ``traffic`` reads two
@@ -175,7 +175,7 @@ def _trace_us(dirname: str, key: str = "fwd_kernel") -> float:
     raise SystemExit(f"no {key} in the kernel statistics under {dirname}")
 
 
-def sweep(out_md: str, title: str, commands: str, entries) -> None:
+def sweep(out_md: str, title: str, commands: str, entries, first: str = "variant") -> None:
     """One table row per `label:flop_per_launch:dir[:kernel]`, where dir holds the
     kernel trace and the counter passes of one bench run and kernel (default
     fwd_kernel) names the kernel of the row."""
@@ -202,13 +202,13 @@ def sweep(out_md: str, title: str, commands: str, entries) -> None:
             f"{m.get('SQ_VALU_MFMA_COEXEC_CYCLES', float('nan')) / max(busy * 1024, 1):.0%}",
             f"{hit / (hit + miss):.1%}",
         ])
-    hdr = ["variant", "kernel us", "TFLOP/s", "MFMA busy cycles per SIMD per us",
+    hdr = [first, "kernel us", "TFLOP/s", "MFMA busy cycles per SIMD per us",
            "VALU / MFMA instr", "exp2 / MFMA", "LDS / MFMA instr", "LDS bank conflict cycles",
            "ready, not issued (of wave cycles)", "waiting", "issuing", "VALU co-issued "
            "beside busy MFMA (of MFMA busy)", "L2 hit rate"]
     lines = [f"# {title}", "", "Commands:", "", commands, "",
              "Kernel time: average of the rocprofv3 kernel trace; counters: means per dispatch of "
-             "separate `--pmc` passes of the same command.  MFMA busy cycles per SIMD per us is the "
+             "separate `--pmc` passes of the same workload.  MFMA busy cycles per SIMD per us is the "
              "busy fraction times the shader clock in MHz (no clock counter is read; at the "
              "~2.0 GHz this load settles at, 1000 = 50%).  The wave-cycle fractions divide "
              "SQ_WAIT_INST_ANY (ready but not issued), SQ_WAIT_ANY (waiting on a dependency, "
@@ -232,7 +232,12 @@ if __name__ == "__main__":
             args = args[1:]
         counters(args[0], args[1], args[2], " ".join(args[3:]), clk)
     elif sys.argv[1] == "sweep":
-        sweep(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5:])
+        args = sys.argv[2:]
+        first = "variant"
+        if args and args[0].startswith("--rows="):
+            first = args[0].split("=", 1)[1]
+            args = args[1:]
+        sweep(args[0], args[1], args[2], args[3:], first)
     elif sys.argv[1] == "traffic":
         traffic(sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5]), sys.argv[6], sys.argv[7],
                 " ".join(sys.argv[8:]))
