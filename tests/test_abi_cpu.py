@@ -62,6 +62,19 @@ def test_launching_entry_points_reject_bad_arguments_before_any_hip_call():
     assert bytes(buf) == b"\0" * len(buf)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_longest_head_accepted_is_just_under_2_31_bytes(d):
+    """One head of one tensor may hold at most 2^31 - 1 bytes (the kernels' byte
+    offsets within a head are 32-bit): N = 2^31 / (2 d) - 1 rows pass the host
+    checks, one more row is ATTN_E_SHAPE.  No memory is touched (host-only check)."""
+    lib = ea.lib()
+    G = 1 << 36  # far-apart addresses, so that no overlap is reported
+    Q, K, V, O, L = (G * (i + 1) for i in range(5))
+    n_max = (1 << 31) // (2 * d) - 1
+    assert lib.attn_fwd_check(1, Q, K, V, O, L, 1, 1, n_max, d, 0.1, 2, 64, 0) == 0
+    assert lib.attn_fwd_check(1, Q, K, V, O, L, 1, 1, n_max + 1, d, 0.1, 2, 64, 0) == 2
+
+
 def test_grouped_and_packed_entry_points_reject_bad_arguments_before_any_hip_call():
     lib = ea.lib()
     buf = ctypes.create_string_buffer(1 << 16)

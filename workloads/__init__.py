@@ -15,6 +15,10 @@ Recipe (the same for every workload):
     (b, h), b-major then h, uniformly without replacement from the same
     generator, and multiplies those K rows by 8 (a power of two, so exact).
 
+Inputs too large to draw on the host (the longest head the boundary accepts)
+are drawn on the GPU by torch's seeded Philox generator instead
+(``draw_on_device``), with the same order and rounding.
+
 Grouped-query inputs draw K and V with H_kv heads; packed variable-length inputs
 are [H, T, d] (K, V [H_kv, T, d]) with row offsets from ``packed_offsets`` and
 lengths, for the mixed-length workloads, from ``length_mix`` (log-uniform,
@@ -154,6 +158,25 @@ def draw(B: int, H: int, N: int, d: int, dtype: str, seed: int, *, with_do: bool
                 idx = torch.from_numpy(rows[b, h])
                 kk[b, h, idx] = kk[b, h, idx] * mul
         out["outlier_rows"] = rows
+    return out
+
+
+def draw_on_device(B: int, H: int, N: int, d: int, dtype: str, seed: int, *,
+                   with_do: bool = False, device: str = "cuda") -> dict:
+    """Q, K, V (and dO) drawn on the GPU, for inputs too large to draw on the host.
+
+    torch's seeded device generator (Philox) draws float32 standard normals of
+    shape [B, H, N, d], Q, K, V, dO in that order, each rounded once
+    (nearest-even) to ``dtype``.  Returns device tensors; slices copied to the
+    host feed the oracle, so both sides see the same values.
+    """
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    out = {}
+    for key in ("q", "k", "v") + (("do",) if with_do else ()):
+        x = torch.randn((B, H, N, d), generator=g, device=device, dtype=torch.float32)
+        out[key] = x.to(_TORCH_DTYPES[dtype])
+        del x
     return out
 
 
