@@ -60,3 +60,74 @@ def test_longest_head_forward_and_backward():
         say(f"  rows {a}..{end - 1}: rel fro dQ {errs[0]:.3e} dK {errs[1]:.3e} dV {errs[2]:.3e} "
             f"(bar {bar:.3e})")
         assert max(errs) <= bar, (a, errs, bar)
+
+
+def test_many_short_heads_forward_and_backward():
+    """131,072 heads of 65 rows (two key tiles, the second one row long), causal,
+    d = 128 fp16: 2.18 GB per tensor, so the last heads start past byte 2^31.
+    Every output is finite; heads at the start, the middle and the end are
+    compared with the oracle."""
+    B, H, N, d, dtype = 64, 2048, 65, 128, "f16"
+    scale = 1.0 / math.sqrt(d)
+    say(f"many heads: B{B} H{H} N{N} d{d} {dtype}, causal")
+    inp = draw_on_device(B, H, N, d, dtype, seed=12, with_do=True)
+    q, k, v, do = (inp[x] for x in ("q", "k", "v", "do"))
+    o, lse = ea.attn_fwd(q, k, v, mask="causal", scale=scale)
+    dq, dk, dv = ea.attn_bwd(q, k, v, o, lse, do, mask="causal", scale=scale)
+    torch.cuda.synchronize()
+    for name, t in (("O", o), ("lse", lse), ("dQ", dq), ("dK", dk), ("dV", dv)):
+        assert bool(torch.isfinite(t).all()), name
+    for b, h in ((0, 0), (0, 1), (31, 1023), (32, 0), (63, 2046), (63, 2047)):
+        qh, kh, vh, doh = (to_f64(t[b, h].cpu()) for t in (q, k, v, do))
+        o_ref, l_ref = oracle.forward_rows(np.arange(N), qh, kh, vh, scale, "causal")
+        check_fwd(to_f64(o[b, h].cpu())[None], lse[b, h].cpu().double().numpy()[None],
+                  o_ref[None], l_ref[None], label=f"head ({b}, {h})")
+        ref = oracle.backward_head(qh, kh, vh, doh, scale, "causal")
+        bar = grad_bar(qh, kh, vh, doh, scale, "causal", 0, 0, dtype)
+        errs = [rel_fro(to_f64(g[b, h].cpu()), r) for g, r in zip((dq, dk, dv), ref)]
+        assert max(errs) <= bar, ((b, h), errs, bar)
+
+
+def test_decode_over_a_pool_beyond_4_gib():
+    """Paged decoding whose pages lie past byte 2^32 of each pool (5.2 GB pools of
+    40,000 64-key pages x 8 key/value heads): every page of the three sequences is
+    taken from the last 4,000 pages, shuffled, and the rest of the pool is NaN."""
+    n_pages, H, H_kv, page, d, dtype = 40000, 32, 8, 64, 128, "bf16"
+    lens = [3000, 64, 1501]
+    scale = 1.0 / math.sqrt(d)
+    say(f"decode, pools of {n_pages} pages ({n_pages * H_kv * page * d * 2 / 1e9:.1f} GB each)")
+    pool_k = torch.full((n_pages, H_kv, page, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    pool_v = torch.full_like(pool_k, float("nan"))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(13)
+    q = torch.randn((len(lens), H, 1, d), generator=g, device="cuda").to(torch.bfloat16)
+    per = [-(-L // page) for L in lens]
+    rng = np.random.default_rng(13)
+    phys = rng.permutation(np.arange(n_pages - 4000, n_pages))[:sum(per)]
+    assert phys.min() * H_kv * page * d * 2 >= (1 << 32)
+    table = np.zeros((len(lens), max(per)), dtype=np.int32)
+    used = 0
+    for s, n in enumerate(per):
+        table[s, :n] = phys[used:used + n]
+        used += n
+    pages = torch.from_numpy(phys.astype(np.int64)).cuda()
+    pool_k[pages] = torch.randn((len(phys), H_kv, page, d), generator=g, device="cuda").to(
+        torch.bfloat16)
+    pool_v[pages] = torch.randn((len(phys), H_kv, page, d), generator=g, device="cuda").to(
+        torch.bfloat16)
+    bt = torch.from_numpy(table).cuda()
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    o, lse = ea.attn_decode(q, pool_k, pool_v, bt, sl, max(lens), scale=scale)
+    torch.cuda.synchronize()
+    # the oracle reads each sequence's own pages, renumbered 0..
+    O_ref, L_ref = [], []
+    for s, n in enumerate(per):
+        own = torch.from_numpy(table[s, :n].astype(np.int64)).cuda()
+        o_s, l_s = oracle.forward_decode(to_f64(q[s:s + 1].cpu()), to_f64(pool_k[own].cpu()),
+                                         to_f64(pool_v[own].cpu()),
+                                         np.arange(n, dtype=np.int32)[None],
+                                         np.array([lens[s]], dtype=np.int32), scale)
+        O_ref.append(o_s)
+        L_ref.append(l_s)
+    check_fwd(to_f64(o.cpu()), lse.cpu().double().numpy(), np.concatenate(O_ref),
+              np.concatenate(L_ref), label="pool beyond 4 GiB")
