@@ -453,36 +453,54 @@ void bwd_dkdv_kernel(BwdParams p, int n_kblk) {
           }
       }
       uint32_t pk[KB][8], dsk[KB][8];
+      auto form = [&](int kb, int j) {
+        const float p0 = fast_exp2(s[kb][2 * j] * c), p1 = fast_exp2(s[kb][2 * j + 1] * c);
+        pk[kb][j] = Elem<T>::pack2(p0, p1);
+        dsk[kb][j] = Elem<T>::pack2(p0 * dp[kb][2 * j], p1 * dp[kb][2 * j + 1]);
+      };
+      // Block 0's P and dS first; block 1's are formed a pair or two at a
+      // time between block 0's products, so that this vector work runs
+      // beside the matrix cores (with one wavefront per SIMD nothing else
+      // would fill them).
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float p0 = fast_exp2(s[kb][2 * j] * c), p1 = fast_exp2(s[kb][2 * j + 1] * c);
-          pk[kb][j] = Elem<T>::pack2(p0, p1);
-          dsk[kb][j] = Elem<T>::pack2(p0 * dp[kb][2 * j], p1 * dp[kb][2 * j + 1]);
-        }
+      for (int j = 0; j < 8; ++j) form(0, j);
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
-        u32x4_t bp[KB], bs[KB];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          bp[kb] = u32x4_t{pk[kb][h2 * 4 + 0], pk[kb][h2 * 4 + 1], pk[kb][h2 * 4 + 2],
-                           pk[kb][h2 * 4 + 3]};
-          bs[kb] = u32x4_t{dsk[kb][h2 * 4 + 0], dsk[kb][h2 * 4 + 1], dsk[kb][h2 * 4 + 2],
-                           dsk[kb][h2 * 4 + 3]};
-        }
+        u32x4_t ag[DBLK], aq[DBLK];
 #pragma unroll
         for (int db = 0; db < DBLK; ++db) {
-          const u32x4_t ag = rd.trans(gt, db, qb * 2 + h2), aq = rd.trans(qt, db, qb * 2 + h2);
+          ag[db] = rd.trans(gt, db, qb * 2 + h2);
+          aq[db] = rd.trans(qt, db, qb * 2 + h2);
+        }
+        const u32x4_t bp0 = {pk[0][h2 * 4 + 0], pk[0][h2 * 4 + 1], pk[0][h2 * 4 + 2],
+                             pk[0][h2 * 4 + 3]};
+        const u32x4_t bs0 = {dsk[0][h2 * 4 + 0], dsk[0][h2 * 4 + 1], dsk[0][h2 * 4 + 2],
+                             dsk[0][h2 * 4 + 3]};
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb) {
-            if (db == 0) {
-              Elem<T>::template mma_acc<true>(dv[kb * DBLK + db], ag, bp[kb]);
-              Elem<T>::template mma_acc<true>(dk[kb * DBLK + db], aq, bs[kb]);
-            } else {
-              Elem<T>::template mma_acc<false>(dv[kb * DBLK + db], ag, bp[kb]);
-              Elem<T>::template mma_acc<false>(dk[kb * DBLK + db], aq, bs[kb]);
-            }
+        for (int db = 0; db < DBLK; ++db) {
+          if (db == 0) {
+            Elem<T>::template mma_acc<true>(dv[db], ag[db], bp0);
+            Elem<T>::template mma_acc<true>(dk[db], aq[db], bs0);
+          } else {
+            Elem<T>::template mma_acc<false>(dv[db], ag[db], bp0);
+            Elem<T>::template mma_acc<false>(dk[db], aq[db], bs0);
+          }
+#pragma unroll
+          for (int u = 0; u < 4 / DBLK; ++u) form(1, h2 * 4 + db * (4 / DBLK) + u);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        const u32x4_t bp1 = {pk[1][h2 * 4 + 0], pk[1][h2 * 4 + 1], pk[1][h2 * 4 + 2],
+                             pk[1][h2 * 4 + 3]};
+        const u32x4_t bs1 = {dsk[1][h2 * 4 + 0], dsk[1][h2 * 4 + 1], dsk[1][h2 * 4 + 2],
+                             dsk[1][h2 * 4 + 3]};
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db) {
+          if (db == 0) {
+            Elem<T>::template mma_acc<true>(dv[DBLK + db], ag[db], bp1);
+            Elem<T>::template mma_acc<true>(dk[DBLK + db], aq[db], bs1);
+          } else {
+            Elem<T>::template mma_acc<false>(dv[DBLK + db], ag[db], bp1);
+            Elem<T>::template mma_acc<false>(dk[DBLK + db], aq[db], bs1);
           }
         }
       }
