@@ -99,3 +99,33 @@ def test_decode_binding_rejects_misplaced_buffers():
     o, lse = ea.attn_decode(*args, max(lens), workspace=ok)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(o).all())
+
+
+@pytest.mark.parametrize("wname", ["decode_s64h32kv8q1ctx8192d128_bf16_page64",
+                                   "decode_s4h32kv8q1ctx131072d128_bf16_page256"])
+def test_decode_workload_full_size(wname):
+    """The benchmark's decoding workloads at full size, every sequence and head
+    against the oracle (each sequence's own pages gathered from the pool)."""
+    from parity_util import map_heads
+    from workloads import BY_NAME, make_inputs
+    w = BY_NAME[wname]
+    say(f"workload {w.name}: drawing inputs")
+    inp = make_inputs(w)
+    q, k, v, bt, sl = (gpu(inp[x]) for x in ("q", "k", "v", "block_table", "seq_lens"))
+    o, lse = ea.attn_decode(q, k, v, bt, sl, w.N, scale=w.scale)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all())
+    table, lens = inp["block_table"].numpy(), inp["seq_lens"].numpy()
+    say(f"workload {w.name}: oracle over {w.B} sequences")
+
+    def one(s):
+        n_pages = -(-int(lens[s]) // w.page_size)
+        own = torch.from_numpy(table[s, :n_pages].astype(np.int64))
+        return oracle.forward_decode(to_f64(inp["q"][s:s + 1]), to_f64(inp["k"][own]),
+                                     to_f64(inp["v"][own]),
+                                     np.arange(n_pages, dtype=np.int32)[None],
+                                     lens[s:s + 1], w.scale)
+
+    res = map_heads(one, list(range(w.B)))
+    check_fwd(to_f64(o.cpu()), lse.cpu().double().numpy(), np.concatenate([r[0] for r in res]),
+              np.concatenate([r[1] for r in res]), label=w.name)
