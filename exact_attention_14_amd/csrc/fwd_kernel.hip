@@ -39,10 +39,14 @@
 //   against the running max m as it stands, without taking the tile's own
 //   row max.  If none of them exceeds 2^kTau (checked through the lane's sum
 //   of them, an upper bound) they are kept: m need not be the exact max, since
-//   it cancels between the numerator and l.  kTau is as large as the 16-bit
-//   type allows: 15 for fp16 (2^15 < 65504), 64 for bf16, whose rounding is
-//   2^-9 relative at any magnitude up to 2^127 (with 2^64 per probability the
-//   fp32 sums stay far below their range).  Otherwise (and while a row has no
+//   it cancels between the numerator and l.  kTau bounds what a kept
+//   probability may add to the fp32 accumulators: 15 for fp16 (2^15 < 65504,
+//   the largest fp16 probability), 32 for bf16 (whose rounding is 2^-9
+//   relative at any magnitude): a tile then adds at most 2^33 |v| per row to
+//   acc, so acc stays finite for |V| up to 2^78 at the longest head (2^17
+//   tiles), where an exact max allows 2^105.  (A bound of 2^64 ran 0.6%
+//   faster on causal attention with outlier keys but overflows for |V|
+//   beyond 2^46.)  Otherwise (and while a row has no
 //   m yet) the exact tile max is taken, m is raised to it, the accumulator, l
 //   and l~ are rescaled (P1 §2.3: the rescale corrects history when the max
 //   moves) and the tile's probabilities are formed again.  Nearly every tile
@@ -72,9 +76,13 @@ namespace attn {
 namespace {
 
 // 2^kTau, the bound on a probability formed against the running max (see the
-// file comment): kTau = 15 for fp16, 64 for bf16.
+// file comment): kTau = 15 for fp16, ATTN_FWD_BF16_TAU (32) for bf16.
+#ifndef ATTN_FWD_BF16_TAU
+#define ATTN_FWD_BF16_TAU 32
+#endif
+constexpr float pow2f(int n) { return n == 0 ? 1.0f : 2.0f * pow2f(n - 1); }
 template <typename T>
-constexpr float kSumBound = std::is_same<T, _Float16>::value ? 32768.0f : 18446744073709551616.0f;
+constexpr float kSumBound = std::is_same<T, _Float16>::value ? pow2f(15) : pow2f(ATTN_FWD_BF16_TAU);
 
 // Work queues of the persistent forward (fwd_kernel with PERSIST): the next unclaimed
 // slot of each die's run of work items, and the number of workgroups that

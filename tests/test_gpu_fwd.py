@@ -67,7 +67,7 @@ def test_outlier_keys_move_the_running_max():
 @pytest.mark.parametrize("mask", [None, "causal"])
 def test_running_max_jumps_beyond_the_optimistic_bound(dtype, mask):
     """Scores that rise in steps far larger than the optimistic bound on a
-    probability (2^64 for bf16, 2^15 for fp16, in exp2 units): every step must
+    probability (2^32 for bf16, 2^15 for fp16, in exp2 units): every step must
     take the exact-max path (a probability formed against the old max would
     overflow), and smaller steps below the bound must not disturb the result.
     Q rows are all e_0 and K's first column rises in steps within and across
@@ -200,3 +200,31 @@ def test_binding_checks_lse_and_workspace():
     g2 = ea.attn_bwd(q, k, v, o, lse, do)
     torch.cuda.synchronize()
     assert all(torch.equal(a, b) for a, b in zip(g1, g2))
+
+
+def test_large_values_after_a_max_jump_stay_finite():
+    """bf16 V of magnitude 2^70 and one key whose score lies 63.5 (exp2 units)
+    above every earlier key of its row: a probability formed against the old
+    max would be 2^63.5, and 2^63.5 * 2^70 overflows fp32.  The exact result
+    (a convex combination of V rows) is representable; the kernel must take the
+    exact-max path before such a product reaches the accumulator."""
+    N, d = 1024, 64
+    inp = draw(1, 2, N, d, "bf16", 78)
+    q, k, v = inp["q"].clone(), inp["k"].clone(), inp["v"].clone()
+    q.zero_()
+    q[..., 0] = 1.0
+    k[..., 0] = 0.0
+    k[..., 100, 0] = 44.0  # 44 * log2(e) = 63.5 in exp2 units, scale 1
+    v = v * 2.0 ** 70       # a power of two: exact in bf16
+    for mask in (None, "causal"):
+        o, lse = run_fwd({"q": q, "k": k, "v": v}, mask, 1.0)
+        assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(lse).all()), mask
+        name, wl, wr = oracle_mask(mask)
+        O_ref = np.empty((2, N, d))
+        L_ref = np.empty((2, N))
+        for h in range(2):
+            O_ref[h], L_ref[h] = oracle.forward_head(to_f64(q[0, h]), to_f64(k[0, h]),
+                                                     to_f64(v[0, h]), 1.0, name, wl, wr)
+        # compare in units of 2^70 (exact rescaling of both sides)
+        check_fwd(to_f64(o[0].cpu()) / 2.0 ** 70, lse[0].cpu().double().numpy(), O_ref / 2.0 ** 70,
+                  L_ref, label=f"|V| ~ 2^70 after a jump, {mask}")
