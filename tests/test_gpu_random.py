@@ -10,7 +10,7 @@ import os
 import numpy as np
 import pytest
 
-from parity_util import GRAD_REL_FRO, bwd_case, fwd_case, say
+from parity_util import bwd_case, fwd_case, say
 
 pytestmark = pytest.mark.gpu
 
