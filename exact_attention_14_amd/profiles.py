@@ -38,14 +38,37 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
+_BOOL_NAMES = {"fwd_kernel": ("pair", "persistent"), "bwd_dq_kernel": ("pair",)}
+_MASK_NAMES = ("none", "causal", "sliding")
+
+
 def _demangle_short(name: str) -> str:
+    """kernel<type,d,mask,flags> from an Itanium-mangled kernel name."""
+    import re
     for key in ("fwd_kernel", "bwd_dq_kernel", "bwd_dkdv_kernel", "bwd_kv_reduce_kernel",
                 "decode_combine_kernel", "decode_kernel"):
         if key in name:
             tail = name.split(key, 1)[1]
-            return key + tail.split("EEvNS")[0].replace("IDF16b", "<bf16,").replace(
-                "IDF16_", "<f16,").replace("Lb1", "pair").replace("Lb0", "").replace(
-                "Li", "").replace("E", ",").replace(",,", ",") + ">"
+            args = []
+            ints = 0
+            bools = []
+            for m in re.finditer(r"DF16b|DF16_|Li(\d+)E|Lb([01])E", tail.split("EEvNS")[0]):
+                t = m.group(0)
+                if t == "DF16b":
+                    args.append("bf16")
+                elif t == "DF16_":
+                    args.append("f16")
+                elif m.group(1) is not None:
+                    ints += 1
+                    v = int(m.group(1))
+                    # the second integer of the attention kernels is the mask mode
+                    args.append(_MASK_NAMES[v] if ints == 2 and key != "decode_combine_kernel"
+                                and v < 3 else str(v))
+                else:
+                    bools.append(m.group(2) == "1")
+            names = _BOOL_NAMES.get(key, ())
+            args += [n for n, b in zip(names, bools) if b]
+            return f"{key}<{','.join(args)}>"
     return name[:60]
 
 
