@@ -49,6 +49,9 @@ float exp2_coeff(float scale) {
   return c < 1e-30f ? 1e-30f : c;
 }
 
+// Windows are read only for a sliding mask and act as unbounded from the
+// head's row count on (for a packed batch, from T on: every sequence is
+// shorter).
 int clip_window(int64_t w, int64_t N) { return static_cast<int>(w < N ? w : N); }
 
 HeadGeom head_geom(const Geometry& g, const int32_t* cu_seqlens) {
@@ -60,9 +63,6 @@ HeadGeom head_geom(const Geometry& g, const int32_t* cu_seqlens) {
   return h;
 }
 
-// Windows are read only for a sliding mask and act as unbounded from the
-// head's row count on (for a packed batch, from T on: every sequence is
-// shorter).
 // Compute units of the current device, looked up once per device.
 std::mutex g_cu_mu;
 int g_cu_count[kMaxDevices];
