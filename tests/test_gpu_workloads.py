@@ -123,3 +123,18 @@ def test_llama13b_causal_forward_backward_f16():
     for name, a, b_ in (("O", o, o2), ("lse", lse, lse2), ("dQ", dq, dq2), ("dK", dk, dk2),
                         ("dV", dv, dv2)):
         assert torch.equal(a, b_), f"{name} differs between two identical calls"
+
+
+@pytest.mark.parametrize("mask", [None, (512, 0)], ids=["none", "sliding512"])
+def test_f16_forward_full_size_all_heads(mask):
+    """The fp16 forward at the headline shape (the fp16 workload is causal):
+    B4 H32 N4096 d128, no mask and a (512, 0) window, every head."""
+    from workloads import draw
+    inp = draw(4, 32, 4096, 128, "f16", seed=23)
+    scale = 1.0 / np.sqrt(128)
+    q, k, v = (gpu(inp[x]) for x in ("q", "k", "v"))
+    o, lse = ea.attn_fwd(q, k, v, mask=mask, scale=scale)
+    torch.cuda.synchronize()
+    name, wl, wr = ("none", 0, 0) if mask is None else ("sliding", mask[0], mask[1])
+    fwd_all_heads(inp, o.cpu(), lse.cpu(), scale, name, wl, wr, row_block=1024 if mask else 0,
+                  label=f"f16 B4 H32 N4096 {name}")
